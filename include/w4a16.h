@@ -1,0 +1,257 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so: W4A16 matmuls over Q4_0 group-32 weights on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (key -> page title; the section is named at each use):
+ *   [RQ] "Repacked QAT Gemma 4 26B-A4B serves on one TPU v6e at 1.9x FP8 throughput"
+ *   [QP] "The Quantization Problem I Didn't Know I Had Until I Tried Running LLMs Locally"
+ *   [WQ] "What quantization really is"
+ *
+ * Number format ([RQ] "A repack, not a re-quantization"): weights are cut into
+ * groups of 32 consecutive values along the input dimension K; each group has
+ * one bf16 scale s and 32 integer levels q in -8..7; the weight is s*q.
+ * Activations stay bf16 and the product accumulates in fp32 ([RQ] "What
+ * changed in vLLM's TPU backend").
+ *
+ * ------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ------------------------------------------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer into caller-owned memory on the
+ *    current HIP device.  The library never allocates, frees or synchronises;
+ *    each call only enqueues kernels on `stream` (0 = the null stream) and
+ *    returns.  Calls are stateless and may be made from several host threads.
+ *  - bf16 values travel as uint16_t bit patterns.
+ *  - Row-major, densely packed unless stated otherwise.
+ *  - The return value is a status code (W4_OK or a negative W4_ERR_*).  Shape
+ *    and pointer checks happen on the host before anything is enqueued; on an
+ *    error nothing is enqueued.  Conditions that depend on the data (non-finite
+ *    inputs, groups off the grid) are reported through device-side outputs,
+ *    because the call returns before the kernels run.
+ *  - Pointers must be 16-byte aligned unless stated otherwise (W4_ERR_ARG).
+ *
+ * ------------------------------------------------------------------------
+ * Packed code layout "tile16" (this library's own layout for gfx950)
+ * ------------------------------------------------------------------------
+ * A logical code matrix q[rows][K] (rows % 16 == 0, K % 32 == 0) is stored in
+ * rows*K/2 bytes.  Each code is its 4-bit two's-complement nibble (q & 0xF).
+ *   G  = K/32 groups per row; row tile t = row/16, r = row%16.
+ *   Tile t occupies bytes [t*8*K, (t+1)*8*K).
+ *   Inside a tile, block b holds groups 4b .. 4b+gb-1 with gb = min(4, G-4b);
+ *   it starts at byte 1024*b and is 256*gb bytes long.
+ *   For the code at column k of group g = 4b+j: chunk c = (k%32)/8, i = k%8,
+ *       byte   = t*8*K + 1024*b + 4*gb*(16*c + r) + 4*j + i/2
+ *       nibble = bits 0..3 if i is even, bits 4..7 if i is odd.
+ * So "lane" 16*c+r of a block owns 4*gb contiguous bytes: the 8 codes of chunk
+ * c of row r for each of the block's groups, which is exactly the operand one
+ * lane feeds to a 16x16x32 bf16 MFMA; a 64-lane wave reads a whole block
+ * (1 KiB for gb = 4) with one 128-bit load per lane.
+ * Scales are bf16 [rows][G], row-major.  MoE weights stack E such matrices:
+ * codes [E][rows*K/2] bytes, scales [E][rows][G].
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  W4_OK = 0,
+  W4_ERR_ARG = -1,       /* null pointer, negative size, misaligned pointer, bad enum */
+  W4_ERR_SHAPE = -2,     /* rows % 16 != 0, K % 32 != 0, or a size out of range */
+  W4_ERR_WORKSPACE = -3, /* workspace pointer null or smaller than required */
+  W4_ERR_HIP = -4        /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Epilogues of w4a16_moe_gmm. */
+enum {
+  W4_EPI_NONE = 0,       /* out[r][n] = acc[r][n]                              */
+  W4_EPI_GEGLU_TANH = 1, /* out[r][n] = bf16(gelu_tanh(bf16(acc[r][n])) * bf16(acc[r][n+N/2])) */
+  W4_EPI_SWIGLU = 2      /* out[r][n] = bf16(silu(bf16(acc[r][n])) * bf16(acc[r][n+N/2]))      */
+};
+
+/* Output element types. */
+enum { W4_OUT_BF16 = 0, W4_OUT_F32 = 1 };
+
+/* Status-code text (static storage). */
+const char* w4a16_status_string(int status);
+
+/* Library ABI version (increments when a signature changes). */
+int w4a16_abi_version(void);
+
+/* Device-side group status values written by q4_group_repack. */
+#define W4_GROUP_OFF_GRID 0u    /* no m in 1..8 reproduced the group */
+#define W4_GROUP_NONFINITE 255u /* the group holds a NaN or an infinity */
+
+/*
+ * q4_group_repack -- recover the Q4_0 grid of bf16 weights and pack them.
+ *
+ * [RQ] "A repack, not a re-quantization"; [QP] "Building the Missing Piece".
+ * For each group of 32 bf16 values w (a = max|w|):
+ *   for m = 1..8: s_m = a/m (fp32, correctly rounded), r_i = w_i/s_m (fp32,
+ *   correctly rounded), q_i = clamp(round-half-even(r_i), -8, 7); accept the
+ *   first m with |r_i - q_i| <= 3/32 for all i.  If none is accepted the codes
+ *   of m = 8 are kept and the group counts as off the grid.  The scale is then
+ *   refined by least squares with the codes fixed, s = sum(w q)/sum(q^2) in
+ *   fp64 (pairwise order: first half plus second half, repeatedly) and rounded
+ *   once to bf16 (nearest, ties to even).
+ *   All-zero group: codes 0, scale +0, status 1.  Any NaN/Inf: codes 0, scale
+ *   0x7FC0 (quiet NaN), status W4_GROUP_NONFINITE.
+ *
+ *   w_bf16    in   [rows][K] bf16
+ *   qweight   out  rows*K/2 bytes, tile16 layout
+ *   scales    out  [rows][K/32] bf16
+ *   group_status  out, nullable  [rows][K/32] uint8: accepted m (1..8),
+ *                 W4_GROUP_OFF_GRID or W4_GROUP_NONFINITE
+ *   counters  in/out, nullable, 8-byte aligned: counters[0] += groups off the
+ *             grid, counters[1] += non-finite groups (the caller zeroes them)
+ * Requires rows % 16 == 0, K % 32 == 0, rows*K < 2^40.
+ */
+int q4_group_repack(const uint16_t* w_bf16, int64_t rows, int64_t K,
+                    uint8_t* qweight, uint16_t* scales, uint8_t* group_status,
+                    unsigned long long* counters, hipStream_t stream);
+
+/*
+ * q4_group_dequant_f32 -- out[n][k] = fp32(scale[n][k/32]) * q[n][k].
+ *
+ * [WQ] "How you actually do it" (dequantize = code times scale).  Runs the
+ * same in-register nibble unpack as the matmul kernels; the product of an
+ * 8-bit and a 4-bit significand is exact in fp32.
+ *   qweight in rows*K/2 bytes tile16; scales in [rows][K/32]; out [rows][K] f32.
+ */
+int q4_group_dequant_f32(const uint8_t* qweight, const uint16_t* scales,
+                         int64_t rows, int64_t K, float* out, hipStream_t stream);
+
+/*
+ * q4_pack_codes -- store logical int8 codes (each in -8..7; other values are
+ * masked to their low 4 bits) in the tile16 layout.  For weights that already
+ * come as codes plus group scales ([RQ] "A repack, not a re-quantization":
+ * the 4-bit container is only a change of storage).
+ *   codes in [rows][K] int8; qweight out rows*K/2 bytes.
+ */
+int q4_pack_codes(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight,
+                  hipStream_t stream);
+
+/*
+ * w4a16_linear -- y = bf16(x . W^T), W[n][k] = s[n][k/32] * q[n][k].
+ *
+ * The W4A16 linear layer ([RQ] "What changed in vLLM's TPU backend"): int4
+ * weights are dequantized on chip, activations stay bf16, products are exact
+ * and accumulate in fp32 (each group's partial sum is scaled by its bf16 scale
+ * in fp32), the output is rounded once to bf16.
+ *   x        in  [M][K] bf16
+ *   qweight  in  N*K/2 bytes tile16; scales in [N][K/32] bf16
+ *   y        out [M][N] bf16
+ * Requires N % 16 == 0, K % 32 == 0, M >= 0 (M == 0 enqueues nothing).
+ */
+int w4a16_linear(const uint16_t* x, int64_t M, int64_t K,
+                 const uint8_t* qweight, const uint16_t* scales, int64_t N,
+                 uint16_t* y, hipStream_t stream);
+
+/*
+ * w4a16_moe_route -- top-k routing plan of a mixture-of-experts layer.
+ *
+ * The model family routes each token to 8 of 128 experts ([RQ] "The gap at
+ * 26B") and hands the experts' rows to a grouped matmul ([RQ] "What changed in
+ * vLLM's TPU backend").  Softmax over all E logits (fp32); top-k by logit value,
+ * ties to the lower expert id; weights are the softmax probabilities at those
+ * ids (not renormalised).  The T*k routed rows r = t*k + j are grouped by expert
+ * (stable: within an expert they keep increasing r).
+ *   logits         in  [T][E] fp32, finite
+ *   topk_ids       out [T][k] int32
+ *   topk_weights   out [T][k] fp32
+ *   expert_offsets out [E+1] int32, exclusive prefix sum of the per-expert counts
+ *   sorted_rows    out [T*k] int32, sorted position -> routed row r
+ *   sorted_tokens  out [T*k] int32, sorted position -> token r / k
+ *   row_to_sorted  out [T*k] int32, routed row r -> sorted position
+ *   ws, ws_bytes   workspace of at least w4a16_moe_route_workspace(T, E, k) bytes
+ * Requires 1 <= k <= E <= 256, k <= 16, T*k < 2^31.  T == 0 writes only the offsets.
+ */
+size_t w4a16_moe_route_workspace(int64_t T, int32_t E, int32_t k);
+int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
+                    int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                    int32_t* sorted_rows, int32_t* sorted_tokens, int32_t* row_to_sorted,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * w4a16_moe_gmm -- grouped W4A16 matmul over expert row ranges.
+ *
+ * The grouped matmul with one scale per 32-wide group that dequantizes each
+ * weight tile on chip before the multiply ([RQ] "What changed in vLLM's TPU
+ * backend").  For every expert e and every sorted row i in
+ * [expert_offsets[e], expert_offsets[e+1]):
+ *     acc[i][n] = sum_k x[src(i)][k] * s_e[n][k/32] * q_e[n][k]     (fp32)
+ * with src(i) = row_index[i] if row_index is not null, else i.  The epilogue
+ * (W4_EPI_*) maps acc to out[i][.]; with GEGLU/SWIGLU the first N/2 weight rows
+ * are the gate and the last N/2 the up projection and out has N/2 columns.
+ *   x              in  [x_rows][K] bf16
+ *   row_index      in, nullable  [R] int32, each in [0, x_rows)
+ *   expert_offsets in  [E+1] int32, non-decreasing, offsets[0] = 0, offsets[E] = R
+ *   qweight        in  E * N*K/2 bytes (tile16 per expert); scales in [E][N][K/32]
+ *   out            out [R][N] (EPI_NONE) or [R][N/2], of out_dtype
+ * Requires N % 16 == 0 (N % 32 == 0 with a gated epilogue), K % 32 == 0;
+ * out_dtype must be W4_OUT_BF16 for gated epilogues.  Rows outside every
+ * expert range are left untouched.
+ */
+int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index,
+                  const int32_t* expert_offsets, int32_t E, int64_t R, int64_t K, int64_t N,
+                  const uint8_t* qweight, const uint16_t* scales,
+                  int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream);
+
+/*
+ * w4a16_moe_combine -- y[t][n] = bf16( sum_{j<k} w[t][j] * o[row_to_sorted[t*k+j]][n] ),
+ * summed in slot order j = 0..k-1 in fp32.
+ *   o              in  [T*k][N] of o_dtype (W4_OUT_F32 or W4_OUT_BF16)
+ *   row_to_sorted  in  [T*k] int32; topk_weights in [T][k] fp32
+ *   y              out [T][N] bf16
+ * Requires N % 8 == 0.
+ */
+int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sorted,
+                      const float* topk_weights, int64_t T, int32_t k, int64_t N,
+                      uint16_t* y, hipStream_t stream);
+
+/*
+ * w4a16_moe_layer -- one whole mixture-of-experts layer over W4A16 experts:
+ * w4a16_moe_route, then w4a16_moe_gmm over the fused gate/up weights with the
+ * gated epilogue (gather of the token rows fused into the operand loads), then
+ * w4a16_moe_gmm over the down weights (fp32 rows), then w4a16_moe_combine.
+ * Everything is enqueued on `stream` ([RQ] "What changed in vLLM's TPU
+ * backend": the experts method loads the packed int4 weights and the 32-wide
+ * scales itself and routes them to the grouped-matmul backend).
+ *   x       in  [T][d] bf16;  logits in [T][E] fp32
+ *   w1_q    in  E * (2I)*d/2 bytes tile16 (rows [0, I) gate, [I, 2I) up);
+ *   w1_s    in  [E][2I][d/32] bf16
+ *   w2_q    in  E * d*I/2 bytes tile16;  w2_s in [E][d][I/32] bf16
+ *   activation  W4_EPI_GEGLU_TANH or W4_EPI_SWIGLU
+ *   y       out [T][d] bf16
+ *   ws      workspace of at least w4a16_moe_layer_workspace(T, E, k, d, I) bytes,
+ *           16-byte aligned; it holds the routing plan (see w4a16_moe_layer_plan)
+ *           and the intermediate activations
+ * Requires d % 32 == 0, I % 32 == 0 and the w4a16_moe_route limits.
+ */
+size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I);
+int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                    const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                    int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * w4a16_moe_layer_plan -- byte offsets, inside a w4a16_moe_layer workspace, of
+ * the routing plan and intermediates it leaves behind (for inspection):
+ *   out[0] topk_ids [T][k] i32      out[1] topk_weights [T][k] f32
+ *   out[2] expert_offsets [E+1] i32 out[3] sorted_rows [T*k] i32
+ *   out[4] sorted_tokens [T*k] i32  out[5] row_to_sorted [T*k] i32
+ *   out[6] route scratch            out[7] a: gated activations [T*k][I] bf16
+ *   out[8] o: down-projection rows [T*k][d] f32 (sorted order)
+ * Returns W4_ERR_ARG for out == NULL or bad sizes.
+ */
+int w4a16_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[9]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,230 @@
+// extern "C" entry points of libw4a16.so: argument checks on the host, then
+// kernel launches on the caller's stream.  No allocation, no synchronisation.
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "w4a16.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+int check_matrix(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0) return W4_ERR_ARG;
+  if (rows % 16 != 0 || K % 32 != 0) return W4_ERR_SHAPE;
+  if (rows > 0 && K > 0 && rows > ((int64_t)1 << 40) / K) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK: success";
+    case W4_ERR_ARG: return "W4_ERR_ARG: null pointer, negative size, misaligned pointer or bad enum";
+    case W4_ERR_SHAPE: return "W4_ERR_SHAPE: rows % 16 != 0, K % 32 != 0 or a size out of range";
+    case W4_ERR_WORKSPACE: return "W4_ERR_WORKSPACE: workspace missing or too small";
+    case W4_ERR_HIP: return "W4_ERR_HIP: kernel launch failed";
+    default: return "unknown w4a16 status";
+  }
+}
+
+int w4a16_abi_version(void) { return kAbiVersion; }
+
+int q4_group_repack(const uint16_t* w_bf16, int64_t rows, int64_t K, uint8_t* qweight, uint16_t* scales,
+                    uint8_t* group_status, unsigned long long* counters, hipStream_t stream) {
+  int st = check_matrix(rows, K);
+  if (st != W4_OK) return st;
+  if (rows == 0 || K == 0) return W4_OK;
+  if (!w_bf16 || !qweight || !scales) return W4_ERR_ARG;
+  if (!aligned16(w_bf16) || !aligned16(qweight) || !aligned16(scales)) return W4_ERR_ARG;
+  if (counters && !aligned8(counters)) return W4_ERR_ARG;
+  w4::launch_repack(w_bf16, rows, K, qweight, scales, group_status, counters, stream);
+  return launch_status();
+}
+
+int q4_group_dequant_f32(const uint8_t* qweight, const uint16_t* scales, int64_t rows, int64_t K, float* out,
+                         hipStream_t stream) {
+  int st = check_matrix(rows, K);
+  if (st != W4_OK) return st;
+  if (rows == 0 || K == 0) return W4_OK;
+  if (!qweight || !scales || !out) return W4_ERR_ARG;
+  if (!aligned16(qweight) || !aligned16(scales) || !aligned16(out)) return W4_ERR_ARG;
+  w4::launch_dequant(qweight, scales, rows, K, out, stream);
+  return launch_status();
+}
+
+int q4_pack_codes(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight, hipStream_t stream) {
+  int st = check_matrix(rows, K);
+  if (st != W4_OK) return st;
+  if (rows == 0 || K == 0) return W4_OK;
+  if (!codes || !qweight) return W4_ERR_ARG;
+  if (!aligned16(codes) || !aligned16(qweight)) return W4_ERR_ARG;
+  w4::launch_pack(codes, rows, K, qweight, stream);
+  return launch_status();
+}
+
+static int run_gemm(const w4::GemmArgs& a, hipStream_t stream) {
+  // Average rows per expert decides the kernel: weight-streaming (decode) or
+  // LDS-tiled MFMA (prefill).
+  w4::launch_gemm_skinny(a, stream);
+  return launch_status();
+}
+
+int w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight, const uint16_t* scales, int64_t N,
+                 uint16_t* y, hipStream_t stream) {
+  if (M < 0) return W4_ERR_ARG;
+  int st = check_matrix(N, K);
+  if (st != W4_OK) return st;
+  if (M == 0 || N == 0) return W4_OK;
+  if (K == 0) return W4_ERR_SHAPE;
+  if (M > INT32_MAX) return W4_ERR_SHAPE;
+  if (!x || !qweight || !scales || !y) return W4_ERR_ARG;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y)) return W4_ERR_ARG;
+  w4::GemmArgs a{};
+  a.x = x;
+  a.row_index = nullptr;
+  a.offsets = nullptr;
+  a.E = 1;
+  a.R = M;
+  a.K = K;
+  a.N = N;
+  a.qweight = qweight;
+  a.scales = scales;
+  a.epilogue = W4_EPI_NONE;
+  a.out = y;
+  a.out_dtype = W4_OUT_BF16;
+  return run_gemm(a, stream);
+}
+
+size_t w4a16_moe_route_workspace(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return 0;
+  return w4::route_workspace_bytes(T, E, k);
+}
+
+int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                    int32_t* expert_offsets, int32_t* sorted_rows, int32_t* sorted_tokens, int32_t* row_to_sorted,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || k > 16) return W4_ERR_ARG;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (!expert_offsets) return W4_ERR_ARG;
+  if (T > 0) {
+    if (!logits || !topk_ids || !topk_weights || !sorted_rows || !sorted_tokens || !row_to_sorted) return W4_ERR_ARG;
+    if (!ws || ws_bytes < w4::route_workspace_bytes(T, E, k)) return W4_ERR_WORKSPACE;
+  }
+  w4::launch_route(logits, T, E, k, topk_ids, topk_weights, expert_offsets, sorted_rows, sorted_tokens, row_to_sorted,
+                   ws, stream);
+  return launch_status();
+}
+
+int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, const int32_t* expert_offsets,
+                  int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales,
+                  int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream) {
+  if (x_rows < 0 || E < 1 || R < 0) return W4_ERR_ARG;
+  if (epilogue != W4_EPI_NONE && epilogue != W4_EPI_GEGLU_TANH && epilogue != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  if (out_dtype != W4_OUT_BF16 && out_dtype != W4_OUT_F32) return W4_ERR_ARG;
+  if (epilogue != W4_EPI_NONE && out_dtype != W4_OUT_BF16) return W4_ERR_ARG;
+  int st = check_matrix(N, K);
+  if (st != W4_OK) return st;
+  if (epilogue != W4_EPI_NONE && N % 32 != 0) return W4_ERR_SHAPE;
+  if (R >= ((int64_t)1 << 31) || x_rows >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (R == 0 || N == 0) return W4_OK;
+  if (K == 0) return W4_ERR_SHAPE;
+  if (!x || !expert_offsets || !qweight || !scales || !out) return W4_ERR_ARG;
+  if (!row_index && x_rows < R) return W4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(out)) return W4_ERR_ARG;
+  w4::GemmArgs a{};
+  a.x = x;
+  a.row_index = row_index;
+  a.offsets = expert_offsets;
+  a.E = E;
+  a.R = R;
+  a.K = K;
+  a.N = N;
+  a.qweight = qweight;
+  a.scales = scales;
+  a.epilogue = epilogue;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return run_gemm(a, stream);
+}
+
+int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sorted, const float* topk_weights,
+                      int64_t T, int32_t k, int64_t N, uint16_t* y, hipStream_t stream) {
+  if (T < 0 || k < 1 || N < 0) return W4_ERR_ARG;
+  if (o_dtype != W4_OUT_BF16 && o_dtype != W4_OUT_F32) return W4_ERR_ARG;
+  if (N % 8 != 0) return W4_ERR_SHAPE;
+  if (T == 0 || N == 0) return W4_OK;
+  if (!o || !row_to_sorted || !topk_weights || !y) return W4_ERR_ARG;
+  if (!aligned16(o) || !aligned16(y)) return W4_ERR_ARG;
+  w4::launch_combine(o, o_dtype, row_to_sorted, topk_weights, T, k, N, y, stream);
+  return launch_status();
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int w4a16_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[9]) {
+  if (!out || T < 0 || E < 1 || E > 256 || k < 1 || k > E || k > 16 || d < 0 || I < 0) return W4_ERR_ARG;
+  const size_t R = (size_t)T * (size_t)k;
+  size_t off = 0;
+  const size_t sizes[9] = {R * 4, R * 4, (size_t)(E + 1) * 4, R * 4, R * 4, R * 4,
+                           w4::route_workspace_bytes(T, E, k), R * (size_t)I * 2, R * (size_t)d * 4};
+  for (int i = 0; i < 9; ++i) {
+    out[i] = off;
+    off = align256(off + sizes[i]);
+  }
+  return W4_OK;
+}
+
+size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I) {
+  size_t p[9];
+  if (w4a16_moe_layer_plan(T, E, k, d, I, p) != W4_OK) return 0;
+  const size_t R = (size_t)T * (size_t)k;
+  return align256(p[8] + R * (size_t)d * 4);
+}
+
+int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                    const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                    int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (activation != W4_EPI_GEGLU_TANH && activation != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  size_t p[9];
+  int st = w4a16_moe_layer_plan(T, E, k, d, I, p);
+  if (st != W4_OK) return st;
+  if (d % 32 != 0 || I % 32 != 0) return W4_ERR_SHAPE;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (T == 0 || d == 0) return W4_OK;
+  if (I == 0) return W4_ERR_SHAPE;
+  if (!x || !logits || !w1_q || !w1_s || !w2_q || !w2_s || !y) return W4_ERR_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < w4a16_moe_layer_workspace(T, E, k, d, I)) return W4_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + p[0]);
+  float* wts = reinterpret_cast<float*>(base + p[1]);
+  int32_t* offs = reinterpret_cast<int32_t*>(base + p[2]);
+  int32_t* srows = reinterpret_cast<int32_t*>(base + p[3]);
+  int32_t* stoks = reinterpret_cast<int32_t*>(base + p[4]);
+  int32_t* r2s = reinterpret_cast<int32_t*>(base + p[5]);
+  void* rws = base + p[6];
+  uint16_t* act = reinterpret_cast<uint16_t*>(base + p[7]);
+  float* o = reinterpret_cast<float*>(base + p[8]);
+  const int64_t R = T * k;
+  st = w4a16_moe_route(logits, T, E, k, ids, wts, offs, srows, stoks, r2s, rws, p[7] - p[6], stream);
+  if (st != W4_OK) return st;
+  st = w4a16_moe_gmm(x, T, stoks, offs, E, R, d, 2 * I, w1_q, w1_s, activation, act, W4_OUT_BF16, stream);
+  if (st != W4_OK) return st;
+  st = w4a16_moe_gmm(act, R, nullptr, offs, E, R, I, d, w2_q, w2_s, W4_EPI_NONE, o, W4_OUT_F32, stream);
+  if (st != W4_OK) return st;
+  return w4a16_moe_combine(o, W4_OUT_F32, r2s, wts, T, k, d, y, stream);
+}
+
+}  // extern "C"

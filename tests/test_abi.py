@@ -1,0 +1,125 @@
+"""C ABI contract checks that need no GPU: the library loads, exports every
+function include/w4a16.h declares with a matching binding signature, and
+rejects bad arguments on the host (those calls return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import int4_group_quantized_q4_amd as w4
+from int4_group_quantized_q4_amd import _lib
+import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for required in ("q4_group_repack", "w4a16_linear", "w4a16_moe_gmm", "w4a16_moe_route", "w4a16_moe_combine"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = _lib.lib()
+    assert lib.w4a16_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert len(w4.status_string(st)) > 5
+    assert "unknown" in w4.status_string(42)
+
+
+def test_repack_argument_errors():
+    lib = _lib.lib()
+    f = lib.q4_group_repack
+    assert f(FAKE, 16, 33, FAKE, FAKE, None, None, None) == w4.W4_ERR_SHAPE
+    assert f(FAKE, 15, 32, FAKE, FAKE, None, None, None) == w4.W4_ERR_SHAPE
+    assert f(FAKE, -16, 32, FAKE, FAKE, None, None, None) == w4.W4_ERR_ARG
+    assert f(None, 16, 32, FAKE, FAKE, None, None, None) == w4.W4_ERR_ARG
+    assert f(FAKE + 2, 16, 32, FAKE, FAKE, None, None, None) == w4.W4_ERR_ARG
+    assert f(FAKE, 16, 32, FAKE, FAKE, None, FAKE + 4, None) == w4.W4_ERR_ARG
+    assert f(FAKE, 1 << 30, 1 << 12, FAKE, FAKE, None, None, None) == w4.W4_ERR_SHAPE
+    assert f(None, 0, 32, None, None, None, None, None) == w4.W4_OK      # empty: nothing enqueued
+
+
+def test_linear_and_gmm_argument_errors():
+    lib = _lib.lib()
+    assert lib.w4a16_linear(FAKE, 4, 256, FAKE, FAKE, 500, FAKE, None) == w4.W4_ERR_SHAPE
+    assert lib.w4a16_linear(FAKE, 4, 250, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_SHAPE
+    assert lib.w4a16_linear(FAKE, -1, 256, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_ARG
+    assert lib.w4a16_linear(None, 4, 256, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_ARG
+    assert lib.w4a16_linear(FAKE, 0, 256, None, None, 512, None, None) == w4.W4_OK
+    g = lib.w4a16_moe_gmm
+    args = [FAKE, 64, FAKE, FAKE, 128, 512, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16, None]
+    bad = list(args); bad[10] = 7
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[12] = w4.W4_OUT_F32               # gated epilogue needs bf16 out
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[7] = 1424                          # N % 32 != 0 with a gated epilogue
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[2] = None; bad[1] = 100            # no gather and too few x rows
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[3] = None
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[4] = 0
+    assert g(*bad) == w4.W4_ERR_ARG
+
+
+def test_route_combine_layer_argument_errors():
+    lib = _lib.lib()
+    assert lib.w4a16_moe_route_workspace(64, 128, 8) > 0
+    assert lib.w4a16_moe_route_workspace(64, 4, 8) == 0
+    r = lib.w4a16_moe_route
+    assert r(FAKE, 64, 128, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == w4.W4_ERR_WORKSPACE
+    assert r(FAKE, 64, 128, 17, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == w4.W4_ERR_ARG
+    assert r(FAKE, 64, 300, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == w4.W4_ERR_ARG
+    assert r(FAKE, 1 << 28, 128, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == w4.W4_ERR_SHAPE
+    c = lib.w4a16_moe_combine
+    assert c(FAKE, 1, FAKE, FAKE, 64, 8, 2812, FAKE, None) == w4.W4_ERR_SHAPE
+    assert c(FAKE, 5, FAKE, FAKE, 64, 8, 2816, FAKE, None) == w4.W4_ERR_ARG
+    ws = lib.w4a16_moe_layer_workspace(64, 128, 8, 2816, 704)
+    R = 64 * 8
+    assert ws >= R * 704 * 2 + R * 2816 * 4
+    L = lib.w4a16_moe_layer
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws - 1, None) == w4.W4_ERR_WORKSPACE
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, ws, None) == w4.W4_ERR_ARG
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 700, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws, None) == w4.W4_ERR_SHAPE
+
+
+def test_layer_plan_offsets():
+    p = w4.w4a16_moe_layer_plan(64, 128, 8, 2816, 704)
+    assert p[0] == 0 and all(b > a for a, b in zip(p, p[1:])) and all(v % 256 == 0 for v in p)
+
+
+def test_layout_roundtrip_and_documented_offsets():
+    rng = np.random.default_rng(0)
+    for rows, K in [(16, 32), (32, 96), (48, 704), (16, 256), (32, 2816)]:
+        c = rng.integers(-8, 8, (rows, K)).astype(np.int8)
+        p = layout.encode(c)
+        assert np.array_equal(layout.decode(p, rows, K), c)
+    # the worked layout example: row 17 (tile 1, r 1), K = 256, column 37
+    # (group 1 -> block 0, j 1; chunk 0; i 5) -> byte 8*256 + 4*4*(0 + 1) + 4 + 2, high nibble
+    codes = np.zeros((32, 256), dtype=np.int8)
+    codes[17, 37] = -3
+    p = layout.encode(codes)
+    nz = np.nonzero(p)[0]
+    assert list(nz) == [2048 + 16 + 4 + 2] and p[nz[0]] == (0xD << 4)

@@ -1,0 +1,70 @@
+"""GPU parity of w4a16_linear against the oracle (normwise max-rel <= 1e-2,
+RMS-rel <= 2e-3; bit-exact where the exact result is representable)."""
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import int4_group_quantized_q4_amd as w4
+import oracle
+from gpu_util import bf16_dev, bits_host, linear_weights, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_linear(x_bits, packed, scale_bits, N):
+    M, K = x_bits.shape
+    say("[linear] M=%d K=%d N=%d" % (M, K, N))
+    y = w4.linear(bf16_dev(x_bits), to_dev(packed), bf16_dev(scale_bits), N)
+    torch.cuda.synchronize()
+    return bits_host(y)
+
+
+def check_linear(M, K, N, seed, label):
+    rng = gen.rng_for(920, seed)
+    packed, codes, sc = linear_weights(rng, N, K)
+    x = gen.bf16_normal(rng, (M, K))
+    y = run_linear(x, packed, sc, N)
+    ref = oracle.linear(x, codes, sc)
+    ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(y), oracle.bf16_bits_to_f64(ref))
+    say("  %s: max_rel %.2e rms_rel %.2e, bf16-identical %.4f" % (label, mx, rms, np.mean(y == ref)))
+    assert ok, (label, mx, rms)
+
+
+def test_linear_dense_tiny():
+    cfg = gen.DENSE_TINY
+    check_linear(cfg["M"], cfg["K"], cfg["N"], 1, "dense-tiny")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_linear_dense_decode_full_size(M):
+    cfg = gen.DENSE_DECODE
+    check_linear(M, cfg["K"], cfg["N"], 100 + M, "dense-decode M=%d" % M)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 16), (2, 96, 48), (3, 704, 32), (5, 2816, 64), (17, 256, 128),
+                                   (33, 512, 64), (64, 160, 16), (100, 1024, 48), (300, 128, 32)])
+def test_linear_ragged_shapes(M, K, N):
+    check_linear(M, K, N, 200 + M + K + N, "ragged %dx%dx%d" % (M, K, N))
+
+
+def test_linear_exact_integer_case():
+    """Unit scales and small-integer activations: every product and partial sum
+    is an integer below 2^24, so the fp32 result is exact and the bf16 output
+    must be bit-identical to the oracle."""
+    rng = gen.rng_for(920, 5)
+    M, K, N = 8, 512, 256
+    packed, codes, _ = linear_weights(rng, N, K)
+    sc = np.full((N, K // 32), 0x3F80, dtype=np.uint16)
+    x = oracle.bf16_from_f64(rng.integers(-8, 9, (M, K)).astype(np.float64))
+    y = run_linear(x, packed, sc, N)
+    assert np.array_equal(y, oracle.linear(x, codes, sc))
+
+
+def test_linear_empty_M():
+    rng = gen.rng_for(920, 6)
+    packed, _, sc = linear_weights(rng, 32, 64)
+    y = torch.full((0, 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_linear(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), to_dev(packed), bf16_dev(sc), 32, y)
+    torch.cuda.synchronize()

@@ -1,0 +1,158 @@
+"""GPU parity of the MoE path (route, grouped matmul, epilogues, combine, the
+whole layer) against the oracle.  Integer plan outputs are compared exactly;
+floating-point outputs with the normwise tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import int4_group_quantized_q4_amd as w4
+import oracle
+from gpu_util import bf16_dev, bits_host, expert_weights, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check_route(logits, k, label):
+    T, E = logits.shape
+    say("[route] %s T=%d E=%d k=%d" % (label, T, E, k))
+    plan = w4.moe_route(to_dev(logits), k)
+    torch.cuda.synchronize()
+    ref = oracle.route(logits, k)
+    assert np.array_equal(plan["topk_ids"].cpu().numpy(), ref["ids"]), label
+    assert np.array_equal(plan["expert_offsets"].cpu().numpy(), ref["offsets"]), label
+    assert np.array_equal(plan["sorted_rows"].cpu().numpy(), ref["perm"]), label
+    assert np.array_equal(plan["sorted_tokens"].cpu().numpy(), ref["tokens"]), label
+    assert np.array_equal(plan["row_to_sorted"].cpu().numpy(), ref["inv"]), label
+    assert np.allclose(plan["topk_weights"].cpu().numpy(), ref["weights"], rtol=2e-6, atol=1e-9), label
+
+
+def test_route_moe_decode():
+    cfg = gen.MOE_DECODE
+    check_route(gen.router_logits(gen.rng_for(cfg["id"], 3), cfg["T"], cfg["E"]), cfg["k"], "moe-decode")
+
+
+def test_route_moe_prefill_zipf():
+    cfg = gen.MOE_PREFILL
+    logits = gen.router_logits(gen.rng_for(cfg["id"], 3), cfg["T"], cfg["E"], "zipf", cfg["zipf_s"])
+    check_route(logits, cfg["k"], "moe-prefill")
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (37, 16, 3), (33, 256, 16), (5, 8, 8), (300, 64, 1), (1000, 128, 8)])
+def test_route_shapes_and_ties(T, E, k):
+    rng = gen.rng_for(930, T + E + k)
+    logits = gen.router_logits(rng, T, E)
+    logits[0, :] = 0.5                               # a row of ties: ids 0..k-1
+    if T > 3:
+        logits[3, E // 2] = logits[3, 1]
+        logits[2, :] = np.round(logits[2, :])        # many ties
+    check_route(logits, k, "shapes")
+
+
+def test_route_empty():
+    offs = torch.full((129,), -1, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    w4.w4a16_moe_route(torch.empty(0, 128, dtype=torch.float32, device="cuda"), 8, e, e.float(), offs, e, e, e,
+                       torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(offs.abs().sum()) == 0
+
+
+def _gmm_case(E, R, K, N, seed, empty_every=3):
+    rng = gen.rng_for(931, seed)
+    counts = rng.integers(0, 2 * R // E + 1, E)
+    counts[::empty_every] = 0                        # some experts get no rows
+    if counts.sum() == 0:
+        counts[1] = 5
+    R = int(counts.sum())
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    x_rows = max(1, R // 2 + 3)
+    x = gen.bf16_normal(rng, (x_rows, K))
+    row_index = rng.integers(0, x_rows, R).astype(np.int32)
+    packed, codes, sc = expert_weights(rng, E, N, K)
+    return offsets, R, x, row_index, packed, codes, sc
+
+
+@pytest.mark.parametrize("E,R,K,N", [(8, 40, 256, 64), (4, 100, 704, 32), (16, 20, 96, 48), (3, 600, 128, 16)])
+def test_gmm_plain_f32_with_gather(E, R, K, N):
+    offsets, R, x, row_index, packed, codes, sc = _gmm_case(E, R, K, N, E + R + K + N)
+    say("[gmm] E=%d R=%d K=%d N=%d" % (E, R, K, N))
+    out = torch.full((R, N), float("nan"), dtype=torch.float32, device="cuda")
+    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sc),
+                     w4.W4_EPI_NONE, out, w4.W4_OUT_F32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = np.zeros((R, N))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            ref[lo:hi] = oracle.linear_f64(x[row_index[lo:hi]], codes[e], sc[e])
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok and not np.isnan(got).any()
+
+
+@pytest.mark.parametrize("act", [w4.W4_EPI_GEGLU_TANH, w4.W4_EPI_SWIGLU])
+def test_gmm_gated_epilogue(act):
+    E, R, K, N = 6, 90, 256, 128
+    offsets, R, x, row_index, packed, codes, sc = _gmm_case(E, R, K, N, 77 + act)
+    say("[gmm gated] act=%d" % act)
+    out = torch.empty((R, N // 2), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sc),
+                     act, out, w4.W4_OUT_BF16)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(bits_host(out))
+    fn = oracle.gelu_tanh if act == w4.W4_EPI_GEGLU_TANH else oracle.moe.silu
+    ref = np.zeros((R, N // 2))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            h = oracle.bf16_bits_to_f64(oracle.linear(x[row_index[lo:hi]], codes[e], sc[e]))
+            ref[lo:hi] = fn(h[:, :N // 2]) * h[:, N // 2:]
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok
+
+
+def moe_inputs(cfg, seed_base=0):
+    rng = gen.rng_for(cfg["id"], 20 + seed_base)
+    T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
+    x = gen.bf16_normal(rng, (T, d))
+    logits = gen.router_logits(rng, T, E, cfg["router"], cfg.get("zipf_s", 1.1))
+    w1p, w1c, w1s = expert_weights(rng, E, 2 * I, d)
+    w2p, w2c, w2s = expert_weights(rng, E, d, I)
+    return x, logits, (w1p, w1c, w1s), (w2p, w2c, w2s)
+
+
+def check_layer(cfg, label):
+    T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
+    x, logits, (w1p, w1c, w1s), (w2p, w2c, w2s) = moe_inputs(cfg)
+    say("[moe layer] %s T=%d" % (label, T))
+    y, views = w4.moe_layer(bf16_dev(x), to_dev(logits), k, I, to_dev(w1p), bf16_dev(w1s), to_dev(w2p),
+                            bf16_dev(w2s), w4.W4_EPI_GEGLU_TANH)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k, keep=True)
+    assert np.array_equal(views["expert_offsets"].cpu().numpy(), ref["plan"]["offsets"])
+    assert np.array_equal(views["sorted_tokens"].cpu().numpy(), ref["plan"]["tokens"])
+    a_ok, a_mx, a_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(views["a"])),
+                                                oracle.bf16_bits_to_f64(ref["a"]))
+    o_ok, o_mx, o_rms = oracle.within_tolerance(views["o"].cpu().numpy(), ref["o"])
+    y_ok, y_mx, y_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y)),
+                                                oracle.bf16_bits_to_f64(ref["y"]))
+    say("  a: %.2e/%.2e  o: %.2e/%.2e  y: %.2e/%.2e (max_rel/rms_rel)" % (a_mx, a_rms, o_mx, o_rms, y_mx, y_rms))
+    assert a_ok and o_ok and y_ok
+
+
+def test_moe_layer_decode_full_size():
+    check_layer(gen.MOE_DECODE, "moe-decode")
+
+
+def test_moe_layer_small_shapes():
+    cfg = dict(id=940, T=19, d=96, I=64, E=8, k=3, router="normal")
+    check_layer(cfg, "small")
+
+
+def test_moe_layer_prefill_full_size():
+    check_layer(gen.MOE_PREFILL, "moe-prefill")
