@@ -1,0 +1,406 @@
+"""Benchmark of the W4A16 MoE path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole MoE layer: routing (top-8 of 128, expert offsets, token
+sort), the gate/up grouped matmul with the fused GEGLU epilogue, the down
+grouped matmul and the weighted combine, each through its own entry point of
+libw4a16.so on torch's current stream.  Inputs are synthetic and seeded and
+already resident in HBM when the timed region starts.  Three distinct weight
+sets (3 x 428 MB, more than the 256 MB last-level cache) are used in turn so
+that the weight bytes come from HBM.
+
+Workloads (default: moe-decode, with moe-prefill measured in the same run):
+  moe-decode    T=64 tokens, d_model 2816, 128 experts, expert hidden 704, top-8
+  moe-prefill   T=4096 tokens, same experts, Zipf(1.1) expert popularity
+  dense-decode  w4a16_linear, M in {1, 8, 16}, K=4096, N=14336
+  repack        q4_group_repack of 30 layers x 128 experts of on-grid bf16 weights
+  e2e           repack of the 30 layers, then T=256 decode through all 30 layers
+
+Prints ONE JSON line.  value = touched-expert weight bytes per layer / layer
+time (moe-decode); the roofline object is for the dominant kernel (the gate/up
+grouped matmul), timed with HIP events around its launches inside the timed
+region.  cpu_baseline times the CPU oracle (test infrastructure) on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+import int4_group_quantized_q4_amd as w4  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
+EXPERT_W1_BYTES = 1408 * 2816 // 2 + 1408 * 88 * 2   # 2,230,272
+EXPERT_W2_BYTES = 2816 * 704 // 2 + 2816 * 22 * 2    # 1,115,136
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ MoE layer
+class MoeLayerSet:
+    """Several distinct MoE weight sets + inputs resident on the device."""
+
+    def __init__(self, cfg, copies, seed, device):
+        self.cfg = cfg
+        T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
+        self.T, self.d, self.I, self.E, self.k = T, d, I, E, k
+        g = gen.torch_generator(device, seed)
+        self.layers = []
+        for c in range(copies):
+            self.layers.append({
+                "w1q": gen.bytes_uniform_t(g, E * 2 * I * d // 2, device),
+                "w1s": gen.scales_loguniform_t(g, (E, 2 * I, d // 32), device),
+                "w2q": gen.bytes_uniform_t(g, E * d * I // 2, device),
+                "w2s": gen.scales_loguniform_t(g, (E, d, I // 32), device),
+                "x": gen.bf16_normal_t(g, (T, d), device),
+                "logits": gen.router_logits_t(g, T, E, device, cfg["router"], cfg.get("zipf_s", 1.1)),
+            })
+        R = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.ids = torch.empty(T, k, **i32)
+        self.wts = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.offs = torch.empty(E + 1, **i32)
+        self.srows = torch.empty(R, **i32)
+        self.stoks = torch.empty(R, **i32)
+        self.r2s = torch.empty(R, **i32)
+        self.rws = torch.empty(max(16, w4.w4a16_moe_route_workspace(T, E, k)), dtype=torch.uint8, device=device)
+        self.act = torch.empty(R, I, dtype=torch.bfloat16, device=device)
+        self.o = torch.empty(R, d, dtype=torch.float32, device=device)
+        self.y = torch.empty(T, d, dtype=torch.bfloat16, device=device)
+
+    def step(self, c, ev=None):
+        L = self.layers[c]
+        T, d, I, E, k = self.T, self.d, self.I, self.E, self.k
+        R = T * k
+        if ev is not None:
+            ev[0].record()
+        w4.w4a16_moe_route(L["logits"], k, self.ids, self.wts, self.offs, self.srows, self.stoks, self.r2s, self.rws)
+        if ev is not None:
+            ev[1].record()
+        w4.w4a16_moe_gmm(L["x"], self.stoks, self.offs, E, R, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
+                         self.act, w4.W4_OUT_BF16)
+        if ev is not None:
+            ev[2].record()
+        w4.w4a16_moe_gmm(self.act, None, self.offs, E, R, I, d, L["w2q"], L["w2s"], w4.W4_EPI_NONE, self.o,
+                         w4.W4_OUT_F32)
+        if ev is not None:
+            ev[3].record()
+        w4.w4a16_moe_combine(self.o, w4.W4_OUT_F32, self.r2s, self.wts, T, k, d, self.y)
+        if ev is not None:
+            ev[4].record()
+
+    def touched(self, c):
+        """Experts with at least one routed row in copy c (host-side, untimed)."""
+        self.step(c)
+        torch.cuda.synchronize()
+        counts = torch.diff(self.offs).cpu().numpy()
+        return int(np.count_nonzero(counts)), counts
+
+
+def time_moe(cfg, steps, warmup, copies=3, seed=1234):
+    dev = torch.device("cuda:0")
+    ls = MoeLayerSet(cfg, copies, seed, dev)
+    touched = [ls.touched(c)[0] for c in range(copies)]
+    for i in range(warmup):
+        ls.step(i % copies)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        ls.step(i % copies, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # route, gmm1, gmm2, combine
+    mean_touched = float(np.mean([touched[i % copies] for i in range(steps)]))
+    return {
+        "ms_per_step": total_ms / steps,
+        "route_ms": float(parts[:, 0].mean()),
+        "gmm1_ms": float(parts[:, 1].mean()),
+        "gmm2_ms": float(parts[:, 2].mean()),
+        "combine_ms": float(parts[:, 3].mean()),
+        "gmm1_ms_p10_p90": [float(np.percentile(parts[:, 1], 10)), float(np.percentile(parts[:, 1], 90))],
+        "touched_experts": mean_touched,
+        "layerset": ls,
+    }
+
+
+def moe_decode_report(steps, warmup):
+    cfg = gen.MOE_DECODE
+    r = time_moe(cfg, steps, warmup)
+    wbytes = r["touched_experts"] * (EXPERT_W1_BYTES + EXPERT_W2_BYTES)
+    w1bytes = r["touched_experts"] * EXPERT_W1_BYTES
+    gmm_ms = r["gmm1_ms"] + r["gmm2_ms"]
+    out = {
+        "value": wbytes / (r["ms_per_step"] * 1e-3) / 1e9,
+        "ms_per_step": r["ms_per_step"],
+        "gmm_weight_GBs": wbytes / (gmm_ms * 1e-3) / 1e9,
+        "gmm_frac_of_hbm": wbytes / (gmm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "weight_bytes_per_layer": wbytes,
+        "touched_experts": r["touched_experts"],
+        "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
+            "achieved": w1bytes / (r["gmm1_ms"] * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": w1bytes / (r["gmm1_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+    }
+    return out, r["layerset"]
+
+
+def moe_prefill_report(steps, warmup):
+    cfg = gen.MOE_PREFILL
+    r = time_moe(cfg, steps, warmup)
+    R = cfg["T"] * cfg["k"]
+    d, I = cfg["d"], cfg["I"]
+    flops1 = 2.0 * R * d * 2 * I
+    flops2 = 2.0 * R * I * d
+    gmm_ms = r["gmm1_ms"] + r["gmm2_ms"]
+    tf = (flops1 + flops2) / (gmm_ms * 1e-3) / 1e12
+    return {
+        "workload": "moe-prefill: T=4096, d_model=2816, E=128, top-8 Zipf(1.1), expert hidden 704, int4 g32",
+        "gmm_TFLOPs": tf,
+        "gmm_frac_of_bf16_mfma": tf / BF16_MFMA_PEAK_TFLOPS,
+        "layer_TFLOPs": (flops1 + flops2) / (r["ms_per_step"] * 1e-3) / 1e12,
+        "ms_per_step": r["ms_per_step"],
+        "useful_flops_per_layer": flops1 + flops2,
+        "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
+            "achieved": flops1 / (r["gmm1_ms"] * 1e-3) / 1e12,
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops1 / (r["gmm1_ms"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "traffic": None,
+        },
+    }
+
+
+def cpu_baseline_decode(layerset):
+    """The oracle (as it stands) on copy 0 of the moe-decode layer: all 64 tokens."""
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import layout
+    L = layerset.layers[0]
+    E, I, d, k, T = layerset.E, layerset.I, layerset.d, layerset.k, layerset.T
+
+    def codes_of(packed, rows, K):
+        byte, shift = layout._index(rows, K)
+        per = packed.cpu().numpy().reshape(E, rows * K // 2)
+        v = (per[:, byte] >> shift[None]) & 0xF
+        return ((v.astype(np.int16) ^ 8) - 8).astype(np.int8)
+
+    w1c = codes_of(L["w1q"], 2 * I, d)
+    w2c = codes_of(L["w2q"], d, I)
+    w1s = L["w1s"].cpu().numpy().view(np.uint16)
+    w2s = L["w2s"].cpu().numpy().view(np.uint16)
+    x = L["x"].view(torch.int16).cpu().numpy().view(np.uint16)
+    logits = L["logits"].cpu().numpy()
+    touched = int(np.count_nonzero(np.bincount(oracle.route(logits, k)["ids"].ravel(), minlength=E)))
+    t0 = time.perf_counter()
+    oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k)
+    dt = time.perf_counter() - t0
+    wbytes = touched * (EXPERT_W1_BYTES + EXPERT_W2_BYTES)
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count()
+    return {
+        "value": wbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "one full moe-decode layer (64 tokens, %d touched experts), NumPy fp64, %.2f s" % (touched, dt),
+    }
+
+
+# ------------------------------------------------------------- dense decode
+def dense_decode_report(steps, warmup):
+    dev = torch.device("cuda:0")
+    cfg = gen.DENSE_DECODE
+    K, N = cfg["K"], cfg["N"]
+    g = gen.torch_generator(dev, 99)
+    copies = 16   # 16 x 33 MB > 256 MB last-level cache
+    qs = [gen.bytes_uniform_t(g, N * K // 2, dev) for _ in range(copies)]
+    ss = [gen.scales_loguniform_t(g, (N, K // 32), dev) for _ in range(copies)]
+    wbytes = N * K // 2 + N * (K // 32) * 2
+    res = {}
+    for M in cfg["Ms"]:
+        x = gen.bf16_normal_t(g, (M, K), dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        for i in range(warmup):
+            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        res["M=%d" % M] = {"us_per_call": ms * 1e3, "weight_GBs": wbytes / (ms * 1e-3) / 1e9,
+                           "frac_of_hbm": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
+# ------------------------------------------------------------------- repack
+def repack_layers(layers, dev, gen_seed=5):
+    """Generate each layer's on-grid bf16 source on the device, repack it and
+    keep only the packed weights.  Returns (packed layers, repack seconds,
+    source bytes, off-grid total)."""
+    cfg = gen.MOE_E2E
+    d, I, E = cfg["d"], cfg["I"], cfg["E"]
+    g = gen.torch_generator(dev, gen_seed)
+    out = []
+    rep_s = 0.0
+    src_bytes = 0
+    off = torch.zeros(2, dtype=torch.int64, device=dev)
+    for l in range(layers):
+        w1, _, _ = gen.ongrid_source_t(g, E * 2 * I, d, *cfg["peak"], dev)
+        w2, _, _ = gen.ongrid_source_t(g, E * d, I, *cfg["peak"], dev)
+        w1q = torch.empty(E * 2 * I * d // 2, dtype=torch.uint8, device=dev)
+        w1s = torch.empty(E * 2 * I, d // 32, dtype=torch.bfloat16, device=dev)
+        w2q = torch.empty(E * d * I // 2, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(E * d, I // 32, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        w4.q4_group_repack(w1, w1q, w1s, None, off)
+        w4.q4_group_repack(w2, w2q, w2s, None, off)
+        b.record()
+        torch.cuda.synchronize()
+        rep_s += a.elapsed_time(b) * 1e-3
+        src_bytes += (w1.numel() + w2.numel()) * 2
+        del w1, w2
+        out.append((w1q, w1s.view(E, 2 * I, d // 32), w2q, w2s.view(E, d, I // 32)))
+    return out, rep_s, src_bytes, int(off[0].item())
+
+
+def repack_report():
+    dev = torch.device("cuda:0")
+    layers, rep_s, src_bytes, off = repack_layers(gen.MOE_E2E["layers"], dev)
+    out_bytes = sum(q.numel() + s.numel() * 2 + q2.numel() + s2.numel() * 2 for q, s, q2, s2 in layers)
+    groups = src_bytes // 64
+    return {"repack_s": rep_s, "groups": groups, "groups_per_s": groups / rep_s,
+            "GBs_read_plus_written": (src_bytes + out_bytes) / rep_s / 1e9, "off_grid_groups": off}
+
+
+def e2e_report(steps, warmup):
+    dev = torch.device("cuda:0")
+    cfg = gen.MOE_E2E
+    T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
+    layers, rep_s, src_bytes, off = repack_layers(cfg["layers"], dev)
+    g = gen.torch_generator(dev, 77)
+    x0 = gen.bf16_normal_t(g, (T, d), dev)
+    logits = [gen.router_logits_t(g, T, E, dev) for _ in layers]
+    ws = torch.empty(w4.w4a16_moe_layer_workspace(T, E, k, d, I), dtype=torch.uint8, device=dev)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+
+    def forward():
+        x = x0
+        for l, (w1q, w1s, w2q, w2s) in enumerate(layers):
+            w4.w4a16_moe_layer(x, logits[l], k, I, w1q, w1s, w2q, w2s, w4.W4_EPI_GEGLU_TANH, y, ws)
+            x = (x.float() + y.float()).to(torch.bfloat16)   # residual (outside the library)
+        return x
+
+    for _ in range(warmup):
+        forward()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        forward()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    wbytes = len(layers) * E * (EXPERT_W1_BYTES + EXPERT_W2_BYTES)
+    return {"decode_ms_per_step_30_layers": ms, "weight_GBs": wbytes / (ms * 1e-3) / 1e9,
+            "repack_s": rep_s, "repack_groups_per_s": (src_bytes // 64) / rep_s, "off_grid_groups": off}
+
+
+# --------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="moe-decode",
+                    choices=["moe-decode", "moe-prefill", "dense-decode", "repack", "e2e"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w4.lib()  # fail loudly if the library is not built
+
+    line = {"metric": "MoE W4A16 GMM: weight-HBM GB/s (decode) and TFLOP/s (prefill), % of roofline",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded), inputs resident in HBM"}
+    if args.workload == "moe-decode":
+        log("moe-decode")
+        rep, ls = moe_decode_report(args.steps, args.warmup)
+        line.update({"value": rep.pop("value"), "unit": "GB/s", "ms_per_step": rep.pop("ms_per_step"),
+                     "dtype": "bf16 x int4 (fp32 accumulate)",
+                     "config": {"workload": "moe-decode: T=64 tokens, d_model=2816, E=128 experts, top-8, "
+                                            "expert hidden 704 (fused gate/up 2816->1408, down 704->2816), "
+                                            "int4 group 32 + bf16 scales", "weight_sets_rotated": 3},
+                     "roofline": rep.pop("roofline")})
+        line["decode"] = rep
+        if not args.no_prefill:
+            log("moe-prefill")
+            pre = moe_prefill_report(max(10, args.steps // 5), max(2, args.warmup // 2))
+            line["prefill"] = pre
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle)")
+            line["cpu_baseline"] = cpu_baseline_decode(ls)
+    elif args.workload == "moe-prefill":
+        pre = moe_prefill_report(args.steps, args.warmup)
+        line.update({"value": pre["gmm_TFLOPs"], "unit": "TFLOP/s", "ms_per_step": pre["ms_per_step"],
+                     "dtype": "bf16 x int4 (fp32 accumulate)", "config": {"workload": pre.pop("workload")},
+                     "roofline": pre.pop("roofline"), "prefill": pre})
+    elif args.workload == "dense-decode":
+        res = dense_decode_report(args.steps, args.warmup)
+        line.update({"value": res["M=16"]["weight_GBs"], "unit": "GB/s", "ms_per_step": res["M=16"]["us_per_call"] / 1e3,
+                     "dtype": "bf16 x int4 (fp32 accumulate)",
+                     "config": {"workload": "dense-decode: w4a16_linear K=4096 N=14336, M in {1,8,16}"},
+                     "dense": res})
+    elif args.workload == "repack":
+        res = repack_report()
+        line.update({"value": res["groups_per_s"], "unit": "groups/s", "ms_per_step": res["repack_s"] * 1e3,
+                     "dtype": "fp32 divide / fp64 least squares",
+                     "config": {"workload": "repack: 30 layers x 128 experts on-grid bf16 (peak level 4..8)"},
+                     "repack": res})
+    else:
+        res = e2e_report(args.steps, args.warmup)
+        line.update({"value": res["weight_GBs"], "unit": "GB/s", "ms_per_step": res["decode_ms_per_step_30_layers"],
+                     "dtype": "bf16 x int4 (fp32 accumulate)",
+                     "config": {"workload": "e2e: repack 30 layers x 128 experts, then T=256 decode through 30 layers"},
+                     "e2e": res})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

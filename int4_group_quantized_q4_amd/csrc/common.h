@@ -37,21 +37,38 @@ __device__ __forceinline__ int64_t tile16_word_offset(int64_t t, int r, int64_t 
   return t * 8 * K + 1024 * b + 4 * gb * (16 * c + r) + 4 * j;
 }
 
+// v_cvt_off_f32_i4 on byte B of a word: the low nibble of that byte, read as a
+// two's-complement 4-bit integer, divided by 16 (exact).  SDWA byte select
+// saves the shift.
+template <int B>
+__device__ __forceinline__ float cvt_i4_byte(uint32_t w) {
+  float r;
+  if constexpr (B == 0) {
+    r = __builtin_amdgcn_cvt_off_f32_i4(w);
+  } else if constexpr (B == 1) {
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  } else if constexpr (B == 2) {
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  } else {
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  }
+  return r;
+}
+
 // Eight codes of one word (code i in bits 4i..4i+3, two's complement) ->
-// eight bf16 values q/16.  v_cvt_off_f32_i4 turns the low nibble of its
-// operand into (signed nibble)/16 exactly; the 1/16 is undone by the caller
-// in fp32 (an exact power-of-two scaling).
+// eight bf16 values q/16, exact: one shift, eight conversions, four packs.
+// The 1/16 is undone by the caller in fp32 (an exact power-of-two scaling).
 __device__ __forceinline__ bf16x8 unpack8_div16(uint32_t w) {
   const uint32_t h = w >> 4;
   bf16x8 r;
-  r[0] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(w);
-  r[1] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(h);
-  r[2] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(w >> 8);
-  r[3] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(h >> 8);
-  r[4] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(w >> 16);
-  r[5] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(h >> 16);
-  r[6] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(w >> 24);
-  r[7] = (__bf16)__builtin_amdgcn_cvt_off_f32_i4(h >> 24);
+  r[0] = (__bf16)cvt_i4_byte<0>(w);
+  r[1] = (__bf16)cvt_i4_byte<0>(h);
+  r[2] = (__bf16)cvt_i4_byte<1>(w);
+  r[3] = (__bf16)cvt_i4_byte<1>(h);
+  r[4] = (__bf16)cvt_i4_byte<2>(w);
+  r[5] = (__bf16)cvt_i4_byte<2>(h);
+  r[6] = (__bf16)cvt_i4_byte<3>(w);
+  r[7] = (__bf16)cvt_i4_byte<3>(h);
   return r;
 }
 
