@@ -62,6 +62,7 @@ class MoeLayerSet:
         for c in range(copies):
             self.layers.append({
                 "w1q": gen.bytes_uniform_t(g, E * 2 * I * d // 2, device),
+                # i.i.d. scales: drawn directly in the tile16 scale layout
                 "w1s": gen.scales_loguniform_t(g, (E, 2 * I, d // 32), device),
                 "w2q": gen.bytes_uniform_t(g, E * d * I // 2, device),
                 "w2s": gen.scales_loguniform_t(g, (E, d, I // 32), device),
@@ -207,12 +208,16 @@ def cpu_baseline_decode(layerset):
         byte, shift = layout._index(rows, K)
         per = packed.cpu().numpy().reshape(E, rows * K // 2)
         v = (per[:, byte] >> shift[None]) & 0xF
-        return ((v.astype(np.int16) ^ 8) - 8).astype(np.int8)
+        return (v.astype(np.int16) - 8).astype(np.int8)
+
+    def scales_of(tiled, rows, K):
+        t = tiled.cpu().numpy().view(np.uint16).reshape(E, -1)
+        return np.stack([layout.decode_scales(t[e], rows, K) for e in range(E)])
 
     w1c = codes_of(L["w1q"], 2 * I, d)
     w2c = codes_of(L["w2q"], d, I)
-    w1s = L["w1s"].cpu().numpy().view(np.uint16)
-    w2s = L["w2s"].cpu().numpy().view(np.uint16)
+    w1s = scales_of(L["w1s"], 2 * I, d)
+    w2s = scales_of(L["w2s"], d, I)
     x = L["x"].view(torch.int16).cpu().numpy().view(np.uint16)
     logits = L["logits"].cpu().numpy()
     touched = int(np.count_nonzero(np.bincount(oracle.route(logits, k)["ids"].ravel(), minlength=E)))

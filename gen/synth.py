@@ -75,8 +75,9 @@ def codes_uniform(rng, shape):
 
 
 def bytes_uniform(rng, nbytes):
-    """Uniform random bytes.  Read as packed two's-complement nibbles these are
-    int4 codes uniform in [-8, 7], whatever the nibble order."""
+    """Uniform random bytes.  Read as packed 4-bit codes (offset-binary
+    nibbles) these are int4 codes uniform in [-8, 7], whatever the nibble
+    order."""
     return rng.integers(0, 256, size=nbytes, dtype=np.uint8)
 
 

@@ -33,20 +33,29 @@
  * Packed code layout "tile16" (this library's own layout for gfx950)
  * ------------------------------------------------------------------------
  * A logical code matrix q[rows][K] (rows % 16 == 0, K % 32 == 0) is stored in
- * rows*K/2 bytes.  Each code is its 4-bit two's-complement nibble (q & 0xF).
+ * rows*K/2 bytes.  Each code is stored offset-binary, u = q + 8 in 0..15.
  *   G  = K/32 groups per row; row tile t = row/16, r = row%16.
  *   Tile t occupies bytes [t*8*K, (t+1)*8*K).
  *   Inside a tile, block b holds groups 4b .. 4b+gb-1 with gb = min(4, G-4b);
  *   it starts at byte 1024*b and is 256*gb bytes long.
- *   For the code at column k of group g = 4b+j: chunk c = (k%32)/8, i = k%8,
- *       byte   = t*8*K + 1024*b + 4*gb*(16*c + r) + 4*j + i/2
- *       nibble = bits 0..3 if i is even, bits 4..7 if i is odd.
+ *   The code at column k of group g = 4b+j (chunk c = (k%32)/8, i = k%8) sits
+ *   in the 32-bit little-endian word at byte
+ *       t*8*K + 1024*b + 4*gb*(16*c + r) + 4*j
+ *   at bit 4*(i/2) + 16*(i%2): the even codes of the chunk fill the low
+ *   half-word, the odd codes the high half-word.
  * So "lane" 16*c+r of a block owns 4*gb contiguous bytes: the 8 codes of chunk
  * c of row r for each of the block's groups, which is exactly the operand one
  * lane feeds to a 16x16x32 bf16 MFMA; a 64-lane wave reads a whole block
- * (1 KiB for gb = 4) with one 128-bit load per lane.
- * Scales are bf16 [rows][G], row-major.  MoE weights stack E such matrices:
- * codes [E][rows*K/2] bytes, scales [E][rows][G].
+ * (1 KiB for gb = 4) with one 128-bit load per lane.  ((word >> 4d) &
+ * 0x000F000F) | 0x43004300 is the bf16 pair (128+u of code 2d, 128+u of code
+ * 2d+1), exact, in one shift and one and-or.
+ * Scales ("tile16" too): the bf16 scale of row n = 16t+r, group g = 4b+j is
+ * element  t*16*G + 64*b + r*gb + j  (gb as above) of a rows*G array, i.e.
+ * for each tile and block the 16 x gb scales sit together, row by row (128
+ * bytes for a full block), so a wave reads one block's scales from one cache
+ * line.  q4_pack_scales converts a plain row-major [rows][G] array.
+ * MoE weights stack E such matrices: codes [E][rows*K/2] bytes, scales
+ * [E][rows*G].
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -104,8 +113,8 @@ int w4a16_abi_version(void);
  *
  *   w_bf16    in   [rows][K] bf16
  *   qweight   out  rows*K/2 bytes, tile16 layout
- *   scales    out  [rows][K/32] bf16
- *   group_status  out, nullable  [rows][K/32] uint8: accepted m (1..8),
+ *   scales    out  rows*K/32 bf16, tile16 scale layout
+ *   group_status  out, nullable  [rows][K/32] uint8 (plain row-major): accepted m (1..8),
  *                 W4_GROUP_OFF_GRID or W4_GROUP_NONFINITE
  *   counters  in/out, nullable, 8-byte aligned: counters[0] += groups off the
  *             grid, counters[1] += non-finite groups (the caller zeroes them)
@@ -121,7 +130,7 @@ int q4_group_repack(const uint16_t* w_bf16, int64_t rows, int64_t K,
  * [WQ] "How you actually do it" (dequantize = code times scale).  Runs the
  * same in-register nibble unpack as the matmul kernels; the product of an
  * 8-bit and a 4-bit significand is exact in fp32.
- *   qweight in rows*K/2 bytes tile16; scales in [rows][K/32]; out [rows][K] f32.
+ *   qweight in rows*K/2 bytes tile16; scales in rows*K/32 tile16; out [rows][K] f32.
  */
 int q4_group_dequant_f32(const uint8_t* qweight, const uint16_t* scales,
                          int64_t rows, int64_t K, float* out, hipStream_t stream);
@@ -137,6 +146,14 @@ int q4_pack_codes(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight
                   hipStream_t stream);
 
 /*
+ * q4_pack_scales -- reorder plain row-major bf16 group scales [rows][K/32]
+ * into the tile16 scale layout (rows*K/32 elements).  Same conditions as
+ * q4_pack_codes.
+ */
+int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* scales_tiled,
+                   hipStream_t stream);
+
+/*
  * w4a16_linear -- y = bf16(x . W^T), W[n][k] = s[n][k/32] * q[n][k].
  *
  * The W4A16 linear layer ([RQ] "What changed in vLLM's TPU backend"): int4
@@ -144,7 +161,7 @@ int q4_pack_codes(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight
  * and accumulate in fp32 (each group's partial sum is scaled by its bf16 scale
  * in fp32), the output is rounded once to bf16.
  *   x        in  [M][K] bf16
- *   qweight  in  N*K/2 bytes tile16; scales in [N][K/32] bf16
+ *   qweight  in  N*K/2 bytes tile16; scales in N*K/32 bf16, tile16 scale layout
  *   y        out [M][N] bf16
  * Requires N % 16 == 0, K % 32 == 0, M >= 0 (M == 0 enqueues nothing).
  */
@@ -191,7 +208,7 @@ int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
  *   x              in  [x_rows][K] bf16
  *   row_index      in, nullable  [R] int32, each in [0, x_rows)
  *   expert_offsets in  [E+1] int32, non-decreasing, offsets[0] = 0, offsets[E] = R
- *   qweight        in  E * N*K/2 bytes (tile16 per expert); scales in [E][N][K/32]
+ *   qweight        in  E * N*K/2 bytes (tile16 per expert); scales in E * N*K/32 (tile16 per expert)
  *   out            out [R][N] (EPI_NONE) or [R][N/2], of out_dtype
  * Requires N % 16 == 0 (N % 32 == 0 with a gated epilogue), K % 32 == 0;
  * out_dtype must be W4_OUT_BF16 for gated epilogues.  Rows outside every
@@ -224,8 +241,8 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
  * scales itself and routes them to the grouped-matmul backend).
  *   x       in  [T][d] bf16;  logits in [T][E] fp32
  *   w1_q    in  E * (2I)*d/2 bytes tile16 (rows [0, I) gate, [I, 2I) up);
- *   w1_s    in  [E][2I][d/32] bf16
- *   w2_q    in  E * d*I/2 bytes tile16;  w2_s in [E][d][I/32] bf16
+ *   w1_s    in  E * 2I*d/32 bf16, tile16 scale layout
+ *   w2_q    in  E * d*I/2 bytes tile16;  w2_s in E * d*I/32 bf16, tile16
  *   activation  W4_EPI_GEGLU_TANH or W4_EPI_SWIGLU
  *   y       out [T][d] bf16
  *   ws      workspace of at least w4a16_moe_layer_workspace(T, E, k, d, I) bytes,

@@ -39,6 +39,7 @@ SIGNATURES = {
     "q4_group_repack": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p, _p]),
     "q4_group_dequant_f32": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
     "q4_pack_codes": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
+    "q4_pack_scales": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
     "w4a16_linear": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
     "w4a16_moe_route_workspace": (_sz, [_i64, _i32, _i32]),
     "w4a16_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),

@@ -75,6 +75,16 @@ int q4_pack_codes(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight
   return launch_status();
 }
 
+int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* scales_tiled, hipStream_t stream) {
+  int st = check_matrix(rows, K);
+  if (st != W4_OK) return st;
+  if (rows == 0 || K == 0) return W4_OK;
+  if (!scales || !scales_tiled) return W4_ERR_ARG;
+  if (!aligned16(scales) || !aligned16(scales_tiled)) return W4_ERR_ARG;
+  w4::launch_pack_scales(scales, rows, K, scales_tiled, stream);
+  return launch_status();
+}
+
 static int run_gemm(const w4::GemmArgs& a, hipStream_t stream) {
   // Average rows per expert decides the kernel: weight-streaming (decode) or
   // LDS-tiled MFMA (prefill).

@@ -37,6 +37,36 @@ __device__ __forceinline__ int64_t tile16_word_offset(int64_t t, int r, int64_t 
   return t * 8 * K + 1024 * b + 4 * gb * (16 * c + r) + 4 * j;
 }
 
+// Element index, inside a tile16 scale array of a matrix with G groups per
+// row, of the scale of row r of tile t, group g (see w4a16.h).
+__device__ __forceinline__ int64_t tile16_scale_index(int64_t t, int r, int64_t g, int64_t G) {
+  const int64_t b = g / kBlockGroups;
+  const int j = (int)(g - b * kBlockGroups);
+  const int64_t rem = G - b * kBlockGroups;
+  const int gb = rem < kBlockGroups ? (int)rem : kBlockGroups;
+  return t * 16 * G + 64 * b + r * gb + j;
+}
+
+// Bit position, inside a tile16 word, of code i (0..7) of a chunk: even codes
+// in the low half-word, odd codes in the high half-word.
+__host__ __device__ constexpr int tile16_bit(int i) { return 4 * (i >> 1) + 16 * (i & 1); }
+
+// Offset-binary nibble u of every code in the word -> bf16 pairs (128 + u of
+// code 2d | 128 + u of code 2d+1 << 16), d = 0..3.  0x4300 is bf16 128.0, whose
+// 7 mantissa bits step by 1, so OR-ing u in gives 128 + u = 136 + q exactly.
+__device__ __forceinline__ u32x4 biased_pairs(uint32_t w) {
+  u32x4 p;
+  p[0] = (w & 0x000F000Fu) | 0x43004300u;
+  p[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  p[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  p[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return p;
+}
+
+// bf16 -136 in every element: the operand that cancels the +136 bias of
+// biased_pairs() through the MFMA's accumulator input.
+constexpr uint32_t kNeg136Pair = 0xC308C308u;
+
 // v_cvt_off_f32_i4 on byte B of a word: the low nibble of that byte, read as a
 // two's-complement 4-bit integer, divided by 16 (exact).  SDWA byte select
 // saves the shift.
@@ -55,26 +85,22 @@ __device__ __forceinline__ float cvt_i4_byte(uint32_t w) {
   return r;
 }
 
-// Eight codes of one word (code i in bits 4i..4i+3, two's complement) ->
-// eight bf16 values q/16, exact: one shift, eight conversions, four packs.
-// The 1/16 is undone by the caller in fp32 (an exact power-of-two scaling).
+// The eight codes of a word as exact bf16 values q/16 (element i = code i).
+// Flipping bit 3 of every nibble turns offset binary into two's complement;
+// v_cvt_off_f32_i4 then gives q/16.  Code i sits in nibble (i/2) + 4*(i%2).
 __device__ __forceinline__ bf16x8 unpack8_div16(uint32_t w) {
-  const uint32_t h = w >> 4;
+  const uint32_t t = w ^ 0x88888888u;
+  const uint32_t h = t >> 4;
   bf16x8 r;
-  r[0] = (__bf16)cvt_i4_byte<0>(w);
-  r[1] = (__bf16)cvt_i4_byte<0>(h);
-  r[2] = (__bf16)cvt_i4_byte<1>(w);
-  r[3] = (__bf16)cvt_i4_byte<1>(h);
-  r[4] = (__bf16)cvt_i4_byte<2>(w);
-  r[5] = (__bf16)cvt_i4_byte<2>(h);
-  r[6] = (__bf16)cvt_i4_byte<3>(w);
-  r[7] = (__bf16)cvt_i4_byte<3>(h);
+  r[0] = (__bf16)cvt_i4_byte<0>(t);   // nibble 0
+  r[1] = (__bf16)cvt_i4_byte<2>(t);   // nibble 4
+  r[2] = (__bf16)cvt_i4_byte<0>(h);   // nibble 1
+  r[3] = (__bf16)cvt_i4_byte<2>(h);   // nibble 5
+  r[4] = (__bf16)cvt_i4_byte<1>(t);   // nibble 2
+  r[5] = (__bf16)cvt_i4_byte<3>(t);   // nibble 6
+  r[6] = (__bf16)cvt_i4_byte<1>(h);   // nibble 3
+  r[7] = (__bf16)cvt_i4_byte<3>(h);   // nibble 7
   return r;
-}
-
-// Signed 4-bit code i of a word, as an integer.
-__device__ __forceinline__ int code_of(uint32_t w, int i) {
-  return ((int)(w << (28 - 4 * i))) >> 28;
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -12,6 +12,7 @@ void launch_repack(const uint16_t* src, int64_t rows, int64_t K, uint8_t* qweigh
 void launch_dequant(const uint8_t* qweight, const uint16_t* scales, int64_t rows, int64_t K,
                     float* out, hipStream_t stream);
 void launch_pack(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight, hipStream_t stream);
+void launch_pack_scales(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst, hipStream_t stream);
 
 // Grouped W4A16 matmul arguments (a dense linear layer is E = 1, no offsets).
 struct GemmArgs {
@@ -22,7 +23,7 @@ struct GemmArgs {
   int64_t R;                 // routed rows
   int64_t K, N;              // weight rows N (before a gated epilogue halves them)
   const uint8_t* qweight;    // E * N*K/2 bytes
-  const uint16_t* scales;    // [E][N][K/32]
+  const uint16_t* scales;    // E * N*K/32, tile16 scale layout
   int32_t epilogue;          // W4_EPI_*
   void* out;
   int32_t out_dtype;         // W4_OUT_*

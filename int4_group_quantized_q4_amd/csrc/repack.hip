@@ -110,9 +110,9 @@ __global__ void __launch_bounds__(256) repack_kernel(
     else if (zero) scale_bits = 0u;
     else scale_bits = f64_to_bf16_rne(num / den);
 
-    // pack: lanes 8c..8c+7 of a half form chunk c's 4-byte word
+    // pack: lanes 8c..8c+7 of a half form chunk c's 4-byte word (offset binary)
     const int qi = (int)q_acc;
-    uint32_t word = ((uint32_t)qi & 0xFu) << (4 * (i & 7));
+    uint32_t word = (uint32_t)(qi + 8) << tile16_bit(i & 7);
     word |= __shfl_xor(word, 1, 64);
     word |= __shfl_xor(word, 2, 64);
     word |= __shfl_xor(word, 4, 64);
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(256) repack_kernel(
         *reinterpret_cast<uint32_t*>(qweight + off) = word;
       }
       if (i == 0) {
-        scales[gid] = (uint16_t)scale_bits;
+        scales[tile16_scale_index(row / kTileRows, (int)(row % kTileRows), g, G)] = (uint16_t)scale_bits;
         if (status_out) status_out[gid] = (uint8_t)status;
       }
     }
@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(
     const int c = (int)(wk & 3);
     const uint32_t word = *reinterpret_cast<const uint32_t*>(
         qweight + tile16_word_offset(n / kTileRows, (int)(n % kTileRows), g, c, K));
-    const float s = bf16_to_f32(scales[n * G + g]);
+    const float s = bf16_to_f32(scales[tile16_scale_index(n / kTileRows, (int)(n % kTileRows), g, G)]);
     const bf16x8 v = unpack8_div16(word);
     float4 lo, hi;
     lo.x = s * ((float)v[0] * 16.0f);
@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(
   }
 }
 
-// One thread per word: 8 int8 codes -> 8 nibbles at their tile16 place.
+// One thread per word: 8 int8 codes -> 8 offset-binary nibbles at their tile16 place.
 __global__ void __launch_bounds__(256) pack_kernel(const int8_t* __restrict__ codes, int64_t rows,
                                                    int64_t K, uint8_t* __restrict__ qweight) {
   const int64_t words_per_row = K / 8;
@@ -184,12 +184,24 @@ __global__ void __launch_bounds__(256) pack_kernel(const int8_t* __restrict__ co
     const uint2 src = *reinterpret_cast<const uint2*>(codes + n * K + wk * 8);
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      word |= ((src.x >> (8 * i)) & 0xFu) << (4 * i);
-      word |= ((src.y >> (8 * i)) & 0xFu) << (4 * (i + 4));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t byte = ((i < 4 ? src.x : src.y) >> (8 * (i & 3))) & 0xFFu;
+      word |= ((byte + 8u) & 0xFu) << tile16_bit(i);   // offset binary of the signed code
     }
     *reinterpret_cast<uint32_t*>(
         qweight + tile16_word_offset(n / kTileRows, (int)(n % kTileRows), wk >> 2, (int)(wk & 3), K)) = word;
+  }
+}
+
+// One thread per scale: plain [rows][G] -> tile16 scale layout.
+__global__ void __launch_bounds__(256) pack_scales_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                          int64_t G, uint16_t* __restrict__ dst) {
+  const int64_t total = rows * G;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = idx / G;
+    const int64_t g = idx - n * G;
+    dst[tile16_scale_index(n / kTileRows, (int)(n % kTileRows), g, G)] = src[idx];
   }
 }
 
@@ -214,6 +226,12 @@ void launch_dequant(const uint8_t* qweight, const uint16_t* scales, int64_t rows
                     float* out, hipStream_t stream) {
   const int grid = grid_for(rows * (K / 8), 256);
   hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(256), 0, stream, qweight, scales, rows, K, out);
+}
+
+void launch_pack_scales(const uint16_t* src, int64_t rows, int64_t K, uint16_t* dst, hipStream_t stream) {
+  const int64_t G = K / kGroup;
+  const int grid = grid_for(rows * G, 256);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(256), 0, stream, src, rows, G, dst);
 }
 
 void launch_pack(const int8_t* codes, int64_t rows, int64_t K, uint8_t* qweight, hipStream_t stream) {

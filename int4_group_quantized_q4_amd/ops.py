@@ -67,6 +67,12 @@ def q4_pack_codes(codes, qweight, stream=None):
     check(st, "q4_pack_codes")
 
 
+def q4_pack_scales(scales, rows, K, scales_tiled, stream=None):
+    st = lib().q4_pack_scales(_ptr(scales, "scales", _BF16_LIKE), rows, K,
+                              _ptr(scales_tiled, "scales_tiled", _BF16_LIKE), _stream(stream))
+    check(st, "q4_pack_scales")
+
+
 def w4a16_linear(x, qweight, scales, N, y, stream=None):
     M, K = x.shape
     st = lib().w4a16_linear(_ptr(x, "x", _BF16_LIKE), M, K, _ptr(qweight, "qweight", (torch.uint8,)),
@@ -131,12 +137,12 @@ def w4a16_moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation, y, ws, 
 
 # -------------------------------------------------------- allocating helpers
 def repack(w, stream=None):
-    """bf16 [rows, K] -> (qweight uint8 [rows*K/2], scales bf16 [rows, K/32],
-    status uint8 [rows, K/32], counters int64 [2])."""
+    """bf16 [rows, K] -> (qweight uint8 [rows*K/2], scales bf16 [rows*K/32]
+    (tile16 scale layout), status uint8 [rows, K/32], counters int64 [2])."""
     rows, K = w.shape
     dev = w.device
     qweight = torch.empty(rows * K // 2, dtype=torch.uint8, device=dev)
-    scales = torch.empty(rows, K // 32, dtype=torch.bfloat16, device=dev)
+    scales = torch.empty(rows * K // 32, dtype=torch.bfloat16, device=dev)
     status = torch.empty(rows, K // 32, dtype=torch.uint8, device=dev)
     counters = torch.zeros(2, dtype=torch.int64, device=dev)
     q4_group_repack(w, qweight, scales, status, counters, stream)
@@ -154,6 +160,14 @@ def pack_codes(codes, stream=None):
     qweight = torch.empty(rows * K // 2, dtype=torch.uint8, device=codes.device)
     q4_pack_codes(codes, qweight, stream)
     return qweight
+
+
+def pack_scales(scales, stream=None):
+    """plain bf16 [rows, K/32] -> tile16 scale layout (flat, rows*K/32)."""
+    rows, G = scales.shape
+    out = torch.empty(rows * G, dtype=scales.dtype, device=scales.device)
+    q4_pack_scales(scales, rows, G * 32, out, stream)
+    return out
 
 
 def linear(x, qweight, scales, N, stream=None):

@@ -33,22 +33,29 @@ def bits_host(t):
 
 
 def linear_weights(rng, N, K):
-    """(packed bytes uint8 [N*K/2], codes int8 [N, K], scale bits uint16 [N, K/32])."""
+    """(packed bytes uint8 [N*K/2], tiled scale bits [N*K/32], codes int8 [N, K],
+    plain scale bits uint16 [N, K/32]).  The first two feed the GPU, the last
+    two the oracle."""
     packed = gen.bytes_uniform(rng, N * K // 2)
     codes = layout.decode(packed, N, K)
     scales = gen.scales_loguniform(rng, (N, K // 32))
-    return packed, codes, scales
+    return packed, layout.encode_scales(scales), codes, scales
 
 
 def expert_weights(rng, E, N, K):
-    """Stacked experts: packed [E*N*K/2], codes int8 [E, N, K], scales [E, N, K/32]."""
+    """Stacked experts: (packed [E*N*K/2], tiled scales [E*N*K/32]) for the GPU,
+    (codes int8 [E, N, K], plain scales [E, N, K/32]) for the oracle."""
     packed = gen.bytes_uniform(rng, E * N * K // 2)
     byte, shift = layout._index(N, K)
     per = packed.reshape(E, N * K // 2)
     v = (per[:, byte] >> shift[None]) & 0xF
-    codes = ((v.astype(np.int16) ^ 8) - 8).astype(np.int8)
+    codes = (v.astype(np.int16) - 8).astype(np.int8)
     scales = gen.scales_loguniform(rng, (E, N, K // 32))
-    return packed, codes, scales
+    tiled = np.empty(E * N * (K // 32), dtype=scales.dtype).reshape(E, -1)
+    idx = layout._scale_index(N, K)
+    for e in range(E):
+        tiled[e, idx] = scales[e]
+    return packed, tiled.reshape(-1), codes, scales
 
 
 def f32_bits_equal(a, b):

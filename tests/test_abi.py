@@ -116,10 +116,18 @@ def test_layout_roundtrip_and_documented_offsets():
         c = rng.integers(-8, 8, (rows, K)).astype(np.int8)
         p = layout.encode(c)
         assert np.array_equal(layout.decode(p, rows, K), c)
-    # the worked layout example: row 17 (tile 1, r 1), K = 256, column 37
-    # (group 1 -> block 0, j 1; chunk 0; i 5) -> byte 8*256 + 4*4*(0 + 1) + 4 + 2, high nibble
-    codes = np.zeros((32, 256), dtype=np.int8)
+    # the documented layout on one code: row 17 (tile 1, r 1), K = 256, column 37
+    # (group 1 -> block 0, j 1; chunk 0; i 5) -> word at 8*256 + 4*4*(16*0 + 1) + 4*1,
+    # bit 4*2 + 16 = 24 -> byte +3, low nibble; offset binary -3 + 8 = 5
+    codes = np.full((32, 256), -8, dtype=np.int8)    # all-zero nibbles
     codes[17, 37] = -3
     p = layout.encode(codes)
     nz = np.nonzero(p)[0]
-    assert list(nz) == [2048 + 16 + 4 + 2] and p[nz[0]] == (0xD << 4)
+    assert list(nz) == [2048 + 16 + 4 + 3] and p[nz[0]] == 0x05
+    # the documented scale position: row 17 (t 1, r 1), K = 704 (G = 22), group 21
+    # (block 5, j 1, gb = 2) -> 1*16*22 + 64*5 + 1*2 + 1
+    sc = np.zeros((32, 22), dtype=np.uint16)
+    sc[17, 21] = 0x3F80
+    ts = layout.encode_scales(sc)
+    assert list(np.nonzero(ts)[0]) == [352 + 320 + 2 + 1]
+    assert np.array_equal(layout.decode_scales(ts, 32, 704), sc)

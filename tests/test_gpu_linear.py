@@ -23,9 +23,9 @@ def run_linear(x_bits, packed, scale_bits, N):
 
 def check_linear(M, K, N, seed, label):
     rng = gen.rng_for(920, seed)
-    packed, codes, sc = linear_weights(rng, N, K)
+    packed, sct, codes, sc = linear_weights(rng, N, K)
     x = gen.bf16_normal(rng, (M, K))
-    y = run_linear(x, packed, sc, N)
+    y = run_linear(x, packed, sct, N)
     ref = oracle.linear(x, codes, sc)
     ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(y), oracle.bf16_bits_to_f64(ref))
     say("  %s: max_rel %.2e rms_rel %.2e, bf16-identical %.4f" % (label, mx, rms, np.mean(y == ref)))
@@ -55,16 +55,16 @@ def test_linear_exact_integer_case():
     must be bit-identical to the oracle."""
     rng = gen.rng_for(920, 5)
     M, K, N = 8, 512, 256
-    packed, codes, _ = linear_weights(rng, N, K)
+    packed, _, codes, _ = linear_weights(rng, N, K)
     sc = np.full((N, K // 32), 0x3F80, dtype=np.uint16)
     x = oracle.bf16_from_f64(rng.integers(-8, 9, (M, K)).astype(np.float64))
-    y = run_linear(x, packed, sc, N)
+    y = run_linear(x, packed, sc.reshape(-1), N)
     assert np.array_equal(y, oracle.linear(x, codes, sc))
 
 
 def test_linear_empty_M():
     rng = gen.rng_for(920, 6)
-    packed, _, sc = linear_weights(rng, 32, 64)
+    packed, sc, _, _ = linear_weights(rng, 32, 64)
     y = torch.full((0, 32), 7.0, dtype=torch.bfloat16, device="cuda")
     w4.w4a16_linear(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), to_dev(packed), bf16_dev(sc), 32, y)
     torch.cuda.synchronize()

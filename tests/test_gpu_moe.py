@@ -71,16 +71,16 @@ def _gmm_case(E, R, K, N, seed, empty_every=3):
     x_rows = max(1, R // 2 + 3)
     x = gen.bf16_normal(rng, (x_rows, K))
     row_index = rng.integers(0, x_rows, R).astype(np.int32)
-    packed, codes, sc = expert_weights(rng, E, N, K)
-    return offsets, R, x, row_index, packed, codes, sc
+    packed, sct, codes, sc = expert_weights(rng, E, N, K)
+    return offsets, R, x, row_index, packed, sct, codes, sc
 
 
 @pytest.mark.parametrize("E,R,K,N", [(8, 40, 256, 64), (4, 100, 704, 32), (16, 20, 96, 48), (3, 600, 128, 16)])
 def test_gmm_plain_f32_with_gather(E, R, K, N):
-    offsets, R, x, row_index, packed, codes, sc = _gmm_case(E, R, K, N, E + R + K + N)
+    offsets, R, x, row_index, packed, sct, codes, sc = _gmm_case(E, R, K, N, E + R + K + N)
     say("[gmm] E=%d R=%d K=%d N=%d" % (E, R, K, N))
     out = torch.full((R, N), float("nan"), dtype=torch.float32, device="cuda")
-    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sc),
+    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
                      w4.W4_EPI_NONE, out, w4.W4_OUT_F32)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
@@ -97,10 +97,10 @@ def test_gmm_plain_f32_with_gather(E, R, K, N):
 @pytest.mark.parametrize("act", [w4.W4_EPI_GEGLU_TANH, w4.W4_EPI_SWIGLU])
 def test_gmm_gated_epilogue(act):
     E, R, K, N = 6, 90, 256, 128
-    offsets, R, x, row_index, packed, codes, sc = _gmm_case(E, R, K, N, 77 + act)
+    offsets, R, x, row_index, packed, sct, codes, sc = _gmm_case(E, R, K, N, 77 + act)
     say("[gmm gated] act=%d" % act)
     out = torch.empty((R, N // 2), dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sc),
+    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
                      act, out, w4.W4_OUT_BF16)
     torch.cuda.synchronize()
     got = oracle.bf16_bits_to_f64(bits_host(out))
@@ -121,17 +121,17 @@ def moe_inputs(cfg, seed_base=0):
     T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
     x = gen.bf16_normal(rng, (T, d))
     logits = gen.router_logits(rng, T, E, cfg["router"], cfg.get("zipf_s", 1.1))
-    w1p, w1c, w1s = expert_weights(rng, E, 2 * I, d)
-    w2p, w2c, w2s = expert_weights(rng, E, d, I)
-    return x, logits, (w1p, w1c, w1s), (w2p, w2c, w2s)
+    w1p, w1t, w1c, w1s = expert_weights(rng, E, 2 * I, d)
+    w2p, w2t, w2c, w2s = expert_weights(rng, E, d, I)
+    return x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s)
 
 
 def check_layer(cfg, label):
     T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
-    x, logits, (w1p, w1c, w1s), (w2p, w2c, w2s) = moe_inputs(cfg)
+    x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s) = moe_inputs(cfg)
     say("[moe layer] %s T=%d" % (label, T))
-    y, views = w4.moe_layer(bf16_dev(x), to_dev(logits), k, I, to_dev(w1p), bf16_dev(w1s), to_dev(w2p),
-                            bf16_dev(w2s), w4.W4_EPI_GEGLU_TANH)
+    y, views = w4.moe_layer(bf16_dev(x), to_dev(logits), k, I, to_dev(w1p), bf16_dev(w1t), to_dev(w2p),
+                            bf16_dev(w2t), w4.W4_EPI_GEGLU_TANH)
     torch.cuda.synchronize()
     ref = oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k, keep=True)
     assert np.array_equal(views["expert_offsets"].cpu().numpy(), ref["plan"]["offsets"])

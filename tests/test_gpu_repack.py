@@ -28,7 +28,7 @@ def run_and_check(w_bits, label):
     ref = oracle.repack_matrix(w_bits)
     codes = layout.decode(q.cpu().numpy(), rows, K)
     assert np.array_equal(codes, ref["codes"]), label
-    assert np.array_equal(bits_host(s), ref["scale"]), label
+    assert np.array_equal(layout.decode_scales(bits_host(s), rows, K), ref["scale"]), label
     assert np.array_equal(st.cpu().numpy(), ref["status"]), label
     c = cnt.cpu().numpy()
     assert int(c[0]) == ref["off_grid"] and int(c[1]) == ref["nonfinite"], label
@@ -98,12 +98,16 @@ def test_repack_realistic_variant_bit_exact():
 
 
 @pytest.mark.parametrize("rows,K", [(16, 32), (32, 96), (48, 704), (1408, 2816)])
-def test_pack_codes_matches_layout(rows, K):
+def test_pack_codes_and_scales_match_layout(rows, K):
     say("[pack] rows=%d K=%d" % (rows, K))
-    codes = gen.codes_uniform(gen.rng_for(911, rows + K), (rows, K))
+    rng = gen.rng_for(911, rows + K)
+    codes = gen.codes_uniform(rng, (rows, K))
+    sc = gen.scales_loguniform(rng, (rows, K // 32))
     q = w4.pack_codes(to_dev(codes))
+    st = w4.pack_scales(bf16_dev(sc))
     torch.cuda.synchronize()
     assert np.array_equal(q.cpu().numpy(), layout.encode(codes))
+    assert np.array_equal(bits_host(st), layout.encode_scales(sc))
 
 
 def test_dequant_random_weights():
@@ -112,6 +116,6 @@ def test_dequant_random_weights():
     codes = gen.codes_uniform(rng, (rows, K))
     sc = gen.scales_loguniform(rng, (rows, K // 32))
     say("[dequant] rows=%d K=%d" % (rows, K))
-    out = w4.dequant(to_dev(layout.encode(codes)), bf16_dev(sc), rows, K)
+    out = w4.dequant(to_dev(layout.encode(codes)), bf16_dev(layout.encode_scales(sc)), rows, K)
     torch.cuda.synchronize()
     assert f32_bits_equal(out.cpu().numpy(), oracle.dequant_f32(codes, sc))
