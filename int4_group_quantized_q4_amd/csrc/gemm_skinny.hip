@@ -7,21 +7,23 @@
 // is", section "Why the tip exists": generation rereads the weights token by
 // token, so this kernel is bound by the weight bytes it streams.
 //
-// Work split: a workgroup of 4 waves serves 4 consecutive work items of one
-// expert; a work item is one 16-row weight tile (two with a gated epilogue:
-// the gate tile and the matching up tile), and its wave streams that tile over
-// the whole K.  The expert's activation rows are staged in LDS chunk by chunk
-// (shared by the 4 waves); the codes and scales of each wave's blocks come
-// straight from global memory through a ring of kPrefetch blocks held in
-// registers (one 128-bit load per lane per 1 KiB tile16 block).
+// Work split: one wave per 16-row weight tile, streaming it over the whole K.
+// A workgroup of 8 waves serves 8 tiles of one expert; with a gated epilogue
+// they are 4 gate/up pairs (wave 2i the gate tile of pair i, wave 2i+1 its up
+// tile) and the up wave hands its accumulator to the gate wave through LDS.
+// The expert's activation rows are staged in LDS in chunks of KC columns,
+// shared by the 8 waves; each wave's codes and scales come straight from global
+// memory through a ring of D blocks held in registers (one 128-bit load per
+// lane per 1 KiB tile16 block, one 64-bit load per lane for its 128 B of
+// scales).
 //
-// Per 4-group block and weight tile: the nibbles become bf16 136+q with one
-// shift and one and-or per pair (biased_pairs); a first MFMA against a
-// constant -136 operand gives -136*sum(x) per row and group, and is the
-// accumulator input of the MFMAs against the biased codes, so each group's
-// partial sum sum(x*q) comes out of the matrix core; the VALU then adds
-// scale * partial into the fp32 accumulator.  Rows beyond the expert's count
-// read a valid row and their results are never stored.
+// Per 4-group block: the nibbles become bf16 136+q with one shift and one
+// and-or per pair (biased_pairs); a first MFMA against a constant -136 operand
+// gives -136*sum(x) per row and group and is the accumulator input of the MFMA
+// against the biased codes, so each group's partial sum sum(x*q) comes out of
+// the matrix core; the VALU adds scale * partial into the fp32 accumulator.
+// Rows beyond the expert's count read a valid row; their results are never
+// stored.
 
 #include "common.h"
 #include "internal.h"
@@ -31,19 +33,19 @@ namespace w4 {
 
 namespace {
 
-// Code/scale blocks in flight per wave, waves (work items) per workgroup, and
-// the occupancy (waves per SIMD) the register allocation aims for (0: none).
-#ifndef W4_DECODE_PREFETCH
-#define W4_DECODE_PREFETCH 4
-#endif
-#ifndef W4_DECODE_WAVES
-#define W4_DECODE_WAVES 4
+constexpr int kWaves = 8;   // waves (weight tiles) per workgroup
+
+// Ring depth of the many-tile (MoE) path and the occupancy its register
+// allocation aims for (waves per SIMD; 0 = compiler default).
+#ifndef W4_DECODE_RING
+#define W4_DECODE_RING 4
 #endif
 #ifndef W4_DECODE_WAVES_PER_SIMD
-#define W4_DECODE_WAVES_PER_SIMD 0
+#define W4_DECODE_WAVES_PER_SIMD 4
 #endif
-constexpr int kPrefetch = W4_DECODE_PREFETCH;
-constexpr int kWaves = W4_DECODE_WAVES;
+#ifndef W4_DECODE_SERIAL
+#define W4_DECODE_SERIAL 0
+#endif
 #if W4_DECODE_WAVES_PER_SIMD > 0
 #define W4_DECODE_OCC __attribute__((amdgpu_waves_per_eu(W4_DECODE_WAVES_PER_SIMD)))
 #else
@@ -67,17 +69,18 @@ __device__ __forceinline__ int xcd_item(int b, int total) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int MAXT, int EPI, int OUT>
+// D: code/scale blocks in flight per wave (ring depth); a chunk of staged
+// activations spans max(4, D) blocks so that ring slots are compile-time.
+template <int MAXT, int EPI, int OUT, int D>
 __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmArgs a, int wg_per_expert,
-                                                                           int total_wg, int items_per_expert) {
+                                                                           int total_wg, int units_per_expert) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
-  constexpr int NW = GATED ? 2 : 1;
-  constexpr int D = kPrefetch;
-  constexpr int KCB = (8 / MAXT) > D ? (8 / MAXT) : D;   // blocks per staged activation chunk
-  constexpr int KC = KCB * 128;          // columns per chunk
-  constexpr int XS = KC * 2 + 16;        // LDS row stride in bytes (padded off the bank period)
-  static_assert(KCB % D == 0, "chunk must hold whole prefetch rounds");
-  __shared__ __align__(16) uint8_t xs[16 * MAXT * XS];
+  constexpr int CB = D > 4 ? D : 4;       // blocks per staged activation chunk
+  constexpr int KC = CB * 128;            // columns per chunk
+  constexpr int XS = KC * 2 + 16;         // LDS row stride in bytes (padded off the bank period)
+  constexpr int XBUF = 16 * MAXT * XS;                       // one staging buffer
+  constexpr int EXBYTES = (kWaves / 2) * MAXT * 64 * 16;     // gate/up hand-over
+  __shared__ __align__(16) uint8_t xs[2 * XBUF > EXBYTES ? 2 * XBUF : EXBYTES];
 
   const int wg = xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
@@ -91,174 +94,215 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nt = wgi * kWaves + wv;
-  const bool active = nt < items_per_expert;   // idle waves still stage and sync
   const int r = lane & 15;
   const int c = lane >> 4;
   const int64_t K = a.K, N = a.N;
+
+  // this wave's weight tile
+  int unit, tile;
+  if constexpr (GATED) {
+    unit = wgi * (kWaves / 2) + (wv >> 1);           // gate/up pair
+    tile = unit + ((wv & 1) ? (int)(N / 32) : 0);    // the up tile sits N/2 rows below
+  } else {
+    unit = wgi * kWaves + wv;
+    tile = unit;
+  }
+  // idle waves (past the expert's last tile) run on tile 0 and store nothing,
+  // so every wave executes the same loads and barriers
+  const bool active = unit < units_per_expert;
+  if (!active) tile = 0;
+
   const int G = (int)(K / kGroup);
   const int NBF = G / kBlockGroups;
   const int gtail = G - NBF * kBlockGroups;
   const int NBall = NBF + (gtail > 0 ? 1 : 0);
+  const uint8_t* wb = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)tile * 8 * K;
+  const uint16_t* sb = a.scales + ((int64_t)e * N + (int64_t)tile * kTileRows) * G;
 
-  const uint8_t* wb[NW];
-  const uint16_t* sb[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int64_t tile = active ? (GATED ? (nt + w * (N / 32)) : nt) : 0;   // up tile: N/2 rows below
-    wb[w] = a.qweight + (int64_t)e * (N * K / 2) + tile * 8 * K;
-    sb[w] = a.scales + ((int64_t)e * N + tile * kTileRows) * G;            // the tile's tile16 scales
-  }
-
-  u32x4 cw[D][NW];
-  u32x2 sw[D][NW];
+  u32x4 cw[D];
+  u32x2 sw[D];
   auto load_block = [&](int slot, int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      cw[slot][w] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb[w] + 1024 * (int64_t)b + 16 * lane));
-      sw[slot][w] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sb[w] + 64 * (int64_t)b + 4 * r));
-    }
+    cw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + 1024 * (int64_t)b + 16 * lane));
+    sw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sb + 64 * (int64_t)b + 4 * r));
   };
 
   // the partial last block (1..3 groups), loaded once
-  uint32_t ct[NW][3] = {};
-  float st[NW][3] = {};
-  if (active && gtail > 0) {
+  uint32_t ct[3] = {0u, 0u, 0u};
+  float st[3] = {0.f, 0.f, 0.f};
+  if (gtail > 0) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < gtail) {
-          ct[w][j] = *reinterpret_cast<const uint32_t*>(wb[w] + 1024 * (int64_t)NBF + 4 * gtail * lane + 4 * j);
-          st[w][j] = bf16_to_f32(sb[w][64 * (int64_t)NBF + r * gtail + j]);
-        }
+    for (int j = 0; j < 3; ++j)
+      if (j < gtail) {
+        ct[j] = *reinterpret_cast<const uint32_t*>(wb + 1024 * (int64_t)NBF + 4 * gtail * lane + 4 * j);
+        st[j] = bf16_to_f32(sb[64 * (int64_t)NBF + r * gtail + j]);
+      }
   }
 
   const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+  // Activation staging: chunk ch (columns [ch*KC, ch*KC+KC)) of the pass's rows
+  // goes to LDS buffer ch%2.  The global loads of chunk ch+1 are issued before
+  // the code loads of chunk ch's blocks and written to LDS after them, so the
+  // (in-order) wait for the activations never drains the code prefetch ring.
+  constexpr int PPR = KC / 8;                       // 16-byte pieces per row of a chunk
+  constexpr int NP = 16 * MAXT * PPR / (64 * kWaves);   // pieces per thread
+  static_assert(NP * 64 * kWaves == 16 * MAXT * PPR, "chunk must split evenly over the threads");
+
   for (int64_t row0 = row_begin; row0 < row_end; row0 += 16 * MAXT) {
     const int cnt = (int)(row_end - row0 < 16 * MAXT ? row_end - row0 : 16 * MAXT);
     const int ntt = (cnt + 15) >> 4;
+    const int nch = (NBall + CB - 1) / CB;
 
-    if (active) {
+    // this thread's staging pieces: source pointers fixed for the pass.  Rows
+    // beyond the count re-read row 0 and columns past K are clamped, so the
+    // loads need no branches; those LDS bytes are never read as operands.
+    const uint16_t* xsrc[NP];
+    int xdst[NP];
+    int xcol[NP];
 #pragma unroll
-      for (int i = 0; i < D; ++i)
-        if (i < NBF) load_block(i, i);
+    for (int q = 0; q < NP; ++q) {
+      const int p = (int)threadIdx.x + q * 64 * kWaves;
+      const int rr = p / PPR;
+      const int pc = p - rr * PPR;
+      const int64_t srow = rr < cnt ? (a.row_index ? (int64_t)a.row_index[row0 + rr] : row0 + rr)
+                                    : (a.row_index ? (int64_t)a.row_index[row0] : row0);
+      xsrc[q] = a.x + srow * K;
+      xdst[q] = rr * XS + pc * 16;
+      xcol[q] = pc * 8;
     }
+    u32x4 xr[NP];
+    auto stage_load = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        int64_t col = (int64_t)ch * KC + xcol[q];
+        col = col < K - 8 ? col : K - 8;
+        xr[q] = *reinterpret_cast<const u32x4*>(xsrc[q] + col);
+      }
+    };
+    auto stage_store = [&](int ch) __attribute__((always_inline)) {
+      uint8_t* buf = xs + (ch & 1) * XBUF;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) *reinterpret_cast<u32x4*>(buf + xdst[q]) = xr[q];
+    };
+
+    __syncthreads();   // the previous pass is done with both buffers
+    stage_load(0);
+    if (NBF > 0) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+    }
+    stage_store(0);
+    __syncthreads();
 
     int arow[MAXT];   // LDS row of this lane's A operand (padding rows read row 0)
 #pragma unroll
     for (int tt = 0; tt < MAXT; ++tt) arow[tt] = (16 * tt + r < cnt) ? 16 * tt + r : 0;
 
-    f32x4 acc[MAXT][NW];
+    f32x4 acc[MAXT];
 #pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt)
-#pragma unroll
-      for (int w = 0; w < NW; ++w) acc[tt][w] = zero4;
+    for (int tt = 0; tt < MAXT; ++tt) acc[tt] = zero4;
 
-    for (int ch = 0; ch * KCB < NBall; ++ch) {
-      // stage activation rows [row0, row0+cnt) x columns [ch*KC, ch*KC + ncol) in LDS
-      __syncthreads();
-      const int col0 = ch * KC;
-      const int ncol = (int)(K - col0 < KC ? K - col0 : KC);
-      const int ppr = ncol >> 3;   // 16-byte pieces per row
-      for (int p = threadIdx.x; p < cnt * ppr; p += 64 * kWaves) {
-        const int rr = p / ppr;
-        const int pc = p - rr * ppr;
-        const int64_t src = a.row_index ? (int64_t)a.row_index[row0 + rr] : row0 + rr;
-        *reinterpret_cast<u32x4*>(xs + rr * XS + pc * 16) =
-            *reinterpret_cast<const u32x4*>(a.x + src * K + col0 + pc * 8);
-      }
-      __syncthreads();
-      if (!active) continue;
-
+    // one block: MFMAs on the slot's codes, then refill the slot with block bn
+    // (after the slot's last use, so no register copies are needed)
+    auto do_block = [&](const uint8_t* xb, int lb, int slot, int bn) __attribute__((always_inline)) {
+      const u32x2 sv = sw[slot];
+      const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16),
+                           bf16_to_f32(sv[1] & 0xFFFFu), bf16_to_f32(sv[1] >> 16)};
 #pragma unroll
-      for (int lb = 0; lb < KCB; ++lb) {
-        const int b = ch * KCB + lb;
-        if (b < NBF) {
-          const int slot = lb % D;
-          bf16x8 A[MAXT][4];
-          f32x4 Cb[MAXT][4];
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 B = as_bf16x8(biased_pairs(cw[slot][j]));
 #pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt)
-            if (tt < ntt) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                A[tt][j] = *reinterpret_cast<const bf16x8*>(xs + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
-                Cb[tt][j] = mfma16x16x32(A[tt][j], as_bf16x8(neg136), zero4);
-              }
-            }
-          f32x4 P[MAXT][NW][4];
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x8 B = as_bf16x8(biased_pairs(cw[slot][w][j]));
-#pragma unroll
-              for (int tt = 0; tt < MAXT; ++tt)
-                if (tt < ntt) P[tt][w][j] = mfma16x16x32(A[tt][j], B, Cb[tt][j]);
-            }
+        for (int tt = 0; tt < MAXT; ++tt)
+          if (tt < ntt) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(xb + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
+            const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+            const f32x4 p = mfma16x16x32(A, B, cb);
+            acc[tt] += sc[j] * p;
           }
-          float sc[NW][4];
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            sc[w][0] = bf16_to_f32(sw[slot][w][0] & 0xFFFFu);
-            sc[w][1] = bf16_to_f32(sw[slot][w][0] >> 16);
-            sc[w][2] = bf16_to_f32(sw[slot][w][1] & 0xFFFFu);
-            sc[w][3] = bf16_to_f32(sw[slot][w][1] >> 16);
-          }
-          if (b + D < NBF) load_block(slot, b + D);
-#pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt)
-            if (tt < ntt) {
-#pragma unroll
-              for (int w = 0; w < NW; ++w)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[tt][w] += sc[w][j] * P[tt][w][j];
-            }
-        }
       }
+      load_block(slot, bn);
+      __builtin_amdgcn_sched_barrier(0);   // issue the refill here, not later
+    };
 
-      if (gtail > 0 && ch == (NBall - 1) / KCB) {
-        const int lb = NBF - ch * KCB;   // local index of the partial block
+    // full chunks: straight-line code, every load unconditional (indices clamped)
+    const int nfull = NBF / CB;
+    for (int ch = 0; ch < nfull; ++ch) {
+      const int chn = ch + 1 < nch ? ch + 1 : nch - 1;
+      stage_load(chn);
+      const uint8_t* xb = xs + (ch & 1) * XBUF;
+#pragma unroll
+      for (int lb = 0; lb < CB; ++lb) {
+        const int bn = ch * CB + lb + D;
+        do_block(xb, lb, lb % D, bn < NBF ? bn : NBF - 1);
+      }
+      stage_store(chn);
+      __syncthreads();
+    }
+    // the last, partial chunk: remaining full blocks and the partial block
+    if (nfull < nch) {
+      const int ch = nfull;
+      const uint8_t* xb = xs + (ch & 1) * XBUF;
+#pragma unroll
+      for (int lb = 0; lb < CB; ++lb)
+        if (ch * CB + lb < NBF) do_block(xb, lb, lb % D, NBF - 1);
+      if (gtail > 0) {
+        const int lb = NBF - ch * CB;   // local index of the partial block
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
           if (j < gtail) {
+            const bf16x8 B = as_bf16x8(biased_pairs(ct[j]));
 #pragma unroll
             for (int tt = 0; tt < MAXT; ++tt)
               if (tt < ntt) {
-                const bf16x8 At = *reinterpret_cast<const bf16x8*>(xs + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
-                const f32x4 cb = mfma16x16x32(At, as_bf16x8(neg136), zero4);
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                  const f32x4 p = mfma16x16x32(At, as_bf16x8(biased_pairs(ct[w][j])), cb);
-                  acc[tt][w] += st[w][j] * p;
-                }
+                const bf16x8 A = *reinterpret_cast<const bf16x8*>(xb + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
+                const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+                const f32x4 p = mfma16x16x32(A, B, cb);
+                acc[tt] += st[j] * p;
               }
           }
         }
       }
+      __syncthreads();
     }
 
-    if (active) {
+    // D rows = 4*(lane/16)+i, column = lane%16
+    if constexpr (GATED) {
+      f32x4* ex = reinterpret_cast<f32x4*>(xs);   // the chunk loop ended with a barrier
+      if (active && (wv & 1)) {
 #pragma unroll
-      for (int tt = 0; tt < MAXT; ++tt) {
-        if (tt >= ntt) continue;
+        for (int tt = 0; tt < MAXT; ++tt) ex[((wv >> 1) * MAXT + tt) * 64 + lane] = acc[tt];
+      }
+      __syncthreads();
+      if (active && !(wv & 1)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = row0 + 16 * tt + 4 * c + i;   // D rows = 4*(lane/16)+i, column = lane%16
-          if (row >= row_end) continue;
-          const int64_t col = (int64_t)nt * kTileRows + r;
-          if constexpr (GATED) {
-            const float g = bf16_to_f32(f32_to_bf16(acc[tt][0][i]));
-            const float u = bf16_to_f32(f32_to_bf16(acc[tt][1][i]));
+        for (int tt = 0; tt < MAXT; ++tt) {
+          if (tt >= ntt) continue;
+          const f32x4 up = ex[((wv >> 1) * MAXT + tt) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = row0 + 16 * tt + 4 * c + i;
+            if (row >= row_end) continue;
+            const float g = bf16_to_f32(f32_to_bf16(acc[tt][i]));
+            const float u = bf16_to_f32(f32_to_bf16(up[i]));
             const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
-            static_cast<uint16_t*>(a.out)[row * (N / 2) + col] = (uint16_t)f32_to_bf16(act * u);
-          } else {
-            const float v = acc[tt][0][i];
-            if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[row * N + col] = v;
-            else static_cast<uint16_t*>(a.out)[row * N + col] = (uint16_t)f32_to_bf16(v);
+            static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)unit * kTileRows + r] =
+                (uint16_t)f32_to_bf16(act * u);
+          }
+        }
+      }
+    } else {
+      if (active) {
+#pragma unroll
+        for (int tt = 0; tt < MAXT; ++tt) {
+          if (tt >= ntt) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = row0 + 16 * tt + 4 * c + i;
+            if (row >= row_end) continue;
+            const int64_t col = (int64_t)tile * kTileRows + r;
+            if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[row * N + col] = acc[tt][i];
+            else static_cast<uint16_t*>(a.out)[row * N + col] = (uint16_t)f32_to_bf16(acc[tt][i]);
           }
         }
       }
@@ -266,34 +310,42 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   }
 }
 
-template <int MAXT>
+template <int MAXT, int D>
 void launch_m(const GemmArgs& a, hipStream_t stream) {
   const bool gated = a.epilogue != W4_EPI_NONE;
-  const int items_per_expert = (int)(gated ? a.N / 32 : a.N / 16);
-  const int wg_per_expert = (items_per_expert + kWaves - 1) / kWaves;
+  const int units = (int)(gated ? a.N / 32 : a.N / 16);
+  const int per_wg = gated ? kWaves / 2 : kWaves;
+  const int wg_per_expert = (units + per_wg - 1) / per_wg;
   const int total = wg_per_expert * a.E;
   dim3 grid(total), block(64 * kWaves);
   if (a.epilogue == W4_EPI_GEGLU_TANH)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_GEGLU_TANH, W4_OUT_BF16>), grid, block, 0, stream, a,
-                       wg_per_expert, total, items_per_expert);
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_GEGLU_TANH, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+                       wg_per_expert, total, units);
   else if (a.epilogue == W4_EPI_SWIGLU)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_SWIGLU, W4_OUT_BF16>), grid, block, 0, stream, a,
-                       wg_per_expert, total, items_per_expert);
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_SWIGLU, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+                       wg_per_expert, total, units);
   else if (a.out_dtype == W4_OUT_F32)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_F32>), grid, block, 0, stream, a,
-                       wg_per_expert, total, items_per_expert);
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_F32, D>), grid, block, 0, stream, a,
+                       wg_per_expert, total, units);
   else
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_BF16>), grid, block, 0, stream, a,
-                       wg_per_expert, total, items_per_expert);
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+                       wg_per_expert, total, units);
 }
 
 }  // namespace
 
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  // rows per expert on average decides how many 16-row MFMA tiles one pass covers
-  const int64_t avg = (a.R + a.E - 1) / a.E;
-  if (avg <= 16) launch_m<1>(a, stream);
-  else launch_m<2>(a, stream);
+  // Fewer waves than SIMDs need a deeper register ring to keep HBM busy.
+  const int64_t tiles = (a.N / 16) * a.E;
+  const int64_t avg = (a.R + a.E - 1) / a.E;   // rows per expert: 16-row MFMA tiles per pass
+  const bool deep = tiles < 4096;
+  if (avg <= 16) {
+    if (deep) launch_m<1, 16>(a, stream);
+    else launch_m<1, W4_DECODE_RING>(a, stream);
+  } else {
+    if (deep) launch_m<2, 8>(a, stream);
+    else launch_m<2, W4_DECODE_RING>(a, stream);
+  }
 }
 
 }  // namespace w4
