@@ -6,16 +6,18 @@
 // token) and section "What changed in vLLM's TPU backend" (the experts' rows
 // are handed to a grouped-matmul backend).
 //
-// Three kernels:
-//  1. topk_rank: a block takes TB tokens (TB*k <= 256 routed rows).  One wave
-//     per token finds the top k logits (ties -> lower id) and the softmax
-//     weights; then the block ranks its TB*k rows within their expert
-//     (ballot-based match inside each wave, prefix over the block's waves) and
-//     writes the per-expert row count of the chunk.
-//  2. scan: one block turns the chunk counts into per-chunk bases and the
-//     expert offsets (exclusive prefix sums).
-//  3. scatter: sorted position = offsets[e] + chunk base + rank in chunk.
-// Rows of one expert keep their original order r = t*k + j (a stable sort).
+// Top-k: one wave per token.  The token's logits go to LDS; every lane ranks
+// its own logits against all E (rank = number of logits that are larger, or
+// equal with a lower id), so the logits with rank < k are the top k and the
+// rank is their slot -- no dependent cross-lane reduction chain.  Softmax
+// max/sum use wave butterflies.
+//
+// Sort: the T*k routed rows r = t*k + j are grouped by expert, keeping r order
+// within an expert.  Small plans (R <= kSmallRows) use one workgroup that
+// counts, ranks, scans and scatters.  Larger plans use chunks of the rows:
+// a kernel ranks each chunk's rows within their expert (ballot-based match
+// inside each wave, prefix over the waves), one block scans the chunk counts
+// into offsets, and a scatter kernel writes the permutation.
 
 #include "common.h"
 #include "internal.h"
@@ -24,83 +26,81 @@ namespace w4 {
 
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kTopkWaves = 8;       // tokens per top-k workgroup
+constexpr int kChunkThreads = 256;  // routed rows per ranking chunk
+constexpr int kSmallRows = 4096;    // single-workgroup sort up to this many rows
+constexpr int kSmallThreads = 1024;
 
-__host__ __device__ inline int tokens_per_block(int k) { return kRouteThreads / k; }
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
-__global__ void __launch_bounds__(kRouteThreads) topk_rank_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ weights, int32_t* __restrict__ chunk_counts, int32_t* __restrict__ rank) {
-  __shared__ int s_ids[kRouteThreads];
-  __shared__ int s_cnt[kRouteThreads / 64][256];
+// One wave per token: ids[t][0..k) by descending logit (ties: lower id first)
+// and their softmax probabilities.
+__global__ void __launch_bounds__(64 * kTopkWaves) topk_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                               int k, int32_t* __restrict__ ids,
+                                                               float* __restrict__ weights) {
+  __shared__ float s_v[kTopkWaves][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int TB = tokens_per_block(k);
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
-  const int nvals = (E + 63) / 64;
-
-  for (int tl = wv; tl < TB; tl += kRouteThreads / 64) {
-    const int64_t t = t0 + tl;
-    if (t >= T) break;
-    float v[4];
-    float mx = -INFINITY;
+  const int64_t t = (int64_t)blockIdx.x * kTopkWaves + wv;
+  if (t >= T) return;   // wave-uniform; no barriers in this kernel
+  float v[4];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = lane + 64 * s;
-      v[s] = (s < nvals && e < E) ? logits[t * E + e] : -INFINITY;
-      mx = fmaxf(mx, v[s]);
-    }
-    mx = wave_max(mx);
-    float sum = 0.0f;
+  for (int s = 0; s < 4; ++s) {
+    const int e = lane + 64 * s;
+    v[s] = e < E ? logits[t * E + e] : -INFINITY;
+    if (e < E) s_v[wv][e] = v[s];
+    mx = fmaxf(mx, v[s]);
+  }
+  mx = wave_max(mx);
+  float sum = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = lane + 64 * s;
-      if (s < nvals && e < E) sum += expf(v[s] - mx);
-    }
+  for (int s = 0; s < 4; ++s)
+    if (lane + 64 * s < E) sum += expf(v[s] - mx);
+  sum = wave_sum(sum);
+  // the wave's LDS writes are visible to the wave after this fence
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int rank[4] = {0, 0, 0, 0};
+  const int E4 = E & ~3;
+  for (int e0 = 0; e0 < E4; e0 += 4) {
+    const float4 w = *reinterpret_cast<const float4*>(&s_v[wv][e0]);
+    const float wvv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    bool taken[4] = {false, false, false, false};
-    for (int j = 0; j < k; ++j) {
-      // best of this lane
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + q;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int e = lane + 64 * s;
-        if (s < nvals && e < E && !taken[s] && (v[s] > bv || (v[s] == bv && e < bi))) {
-          bv = v[s];
-          bi = e;
-        }
-      }
-      // wave argmax, ties -> lower id
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (lane + 64 * s == bi) taken[s] = true;
-      if (lane == 0) {
-        ids[t * k + j] = bi;
-        weights[t * k + j] = expf(bv - mx) / sum;
-        s_ids[tl * k + j] = bi;
+        const int me = lane + 64 * s;
+        rank[s] += (wvv[q] > v[s] || (wvv[q] == v[s] && e < me)) ? 1 : 0;
       }
     }
   }
-  for (int x = threadIdx.x; x < (kRouteThreads / 64) * 256; x += kRouteThreads) (&s_cnt[0][0])[x] = 0;
-  __syncthreads();
+  for (int e = E4; e < E; ++e) {
+    const float w = s_v[wv][e];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int me = lane + 64 * s;
+      rank[s] += (w > v[s] || (w == v[s] && e < me)) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = lane + 64 * s;
+    if (e < E && rank[s] < k) {
+      ids[t * k + rank[s]] = e;
+      weights[t * k + rank[s]] = expf(v[s] - mx) / sum;
+    }
+  }
+}
 
-  // rank each routed row of this chunk within its expert
-  const int64_t rows_here_i = (T - t0) < TB ? (T - t0) * k : (int64_t)TB * k;
-  const int rows_here = (int)rows_here_i;
-  const int rl = threadIdx.x;
-  const bool live = rl < rows_here;
-  const int e = live ? s_ids[rl] : 0x1ff;   // dead lanes use an id no expert has
+// rank of each lane's row among the wave's rows with the same expert id
+// (ids < 512; dead lanes pass 0x1ff), and the size of its id group
+__device__ __forceinline__ void wave_match(int e, int lane, int& rank_in_wave, int& group) {
   uint64_t same = ~0ull;
 #pragma unroll
   for (int bit = 0; bit < 9; ++bit) {
@@ -108,39 +108,120 @@ __global__ void __launch_bounds__(kRouteThreads) topk_rank_kernel(
     same &= ((e >> bit) & 1) ? bal : ~bal;
   }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int rank_in_wave = __popcll(same & lt);
-  if (live && rank_in_wave == 0) s_cnt[wv][e] = __popcll(same);
+  rank_in_wave = __popcll(same & lt);
+  group = __popcll(same);
+}
+
+// One workgroup for the whole plan (R <= kSmallRows).
+__global__ void __launch_bounds__(kSmallThreads) sort_small_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                  int k, int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted_rows,
+                                                                  int32_t* __restrict__ sorted_tokens,
+                                                                  int32_t* __restrict__ row_to_sorted) {
+  constexpr int NW = kSmallThreads / 64;
+  __shared__ int s_cnt[NW][256];   // per-wave counts of the current pass
+  __shared__ int s_base[256];      // rows of each expert seen in earlier passes
+  __shared__ int s_off[257];
+  __shared__ int s_rank[kSmallRows];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int x = tid; x < 256; x += kSmallThreads) s_base[x] = 0;
+  for (int r0 = 0; r0 < R; r0 += kSmallThreads) {
+    for (int x = tid; x < NW * 256; x += kSmallThreads) (&s_cnt[0][0])[x] = 0;
+    __syncthreads();
+    const int r = r0 + tid;
+    const bool live = r < R;
+    const int e = live ? ids[r] : 0x1ff;
+    int rw, grp;
+    wave_match(e, lane, rw, grp);
+    if (live && rw == 0) s_cnt[wv][e] = grp;
+    __syncthreads();
+    if (live) {
+      int before = s_base[e];
+      for (int w = 0; w < wv; ++w) before += s_cnt[w][e];
+      s_rank[r] = before + rw;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kSmallThreads) {
+      int add = 0;
+      for (int w = 0; w < NW; ++w) add += s_cnt[w][x];
+      s_base[x] += add;
+    }
+    __syncthreads();   // the next pass clears s_cnt
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int x = 0; x < E; ++x) {
+      s_off[x] = run;
+      run += s_base[x];
+    }
+    s_off[E] = run;
+  }
+  __syncthreads();
+  for (int x = tid; x <= E; x += kSmallThreads) offsets[x] = s_off[x];
+  for (int r = tid; r < R; r += kSmallThreads) {
+    const int pos = s_off[ids[r]] + s_rank[r];
+    sorted_rows[pos] = r;
+    sorted_tokens[pos] = r / k;
+    row_to_sorted[r] = pos;
+  }
+}
+
+// Large plans, step 1: rank each chunk's rows within their expert.
+__global__ void __launch_bounds__(kChunkThreads) rank_chunks_kernel(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                                    int32_t* __restrict__ chunk_counts,
+                                                                    int32_t* __restrict__ rank) {
+  __shared__ int s_cnt[kChunkThreads / 64][256];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int x = tid; x < (kChunkThreads / 64) * 256; x += kChunkThreads) (&s_cnt[0][0])[x] = 0;
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * kChunkThreads + tid;
+  const bool live = r < R;
+  const int e = live ? ids[r] : 0x1ff;
+  int rw, grp;
+  wave_match(e, lane, rw, grp);
+  if (live && rw == 0) s_cnt[wv][e] = grp;
   __syncthreads();
   if (live) {
     int before = 0;
     for (int w = 0; w < wv; ++w) before += s_cnt[w][e];
-    rank[t0 * k + rl] = before + rank_in_wave;
+    rank[r] = before + rw;
   }
-  for (int ee = threadIdx.x; ee < E; ee += kRouteThreads) {
+  for (int x = tid; x < E; x += kChunkThreads) {
     int total = 0;
 #pragma unroll
-    for (int w = 0; w < kRouteThreads / 64; ++w) total += s_cnt[w][ee];
-    chunk_counts[(int64_t)blockIdx.x * E + ee] = total;
+    for (int w = 0; w < kChunkThreads / 64; ++w) total += s_cnt[w][x];
+    chunk_counts[(int64_t)blockIdx.x * E + x] = total;
   }
 }
 
-// One block: chunk counts -> chunk bases (in place), expert offsets.
+// Large plans, step 2: chunk counts -> chunk bases (in place) and offsets.
 __global__ void __launch_bounds__(256) scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
                                                    int32_t* __restrict__ offsets) {
   __shared__ int s_tot[256];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int c = chunk_counts[(int64_t)ch * E + e];
+    int ch = 0;
+    for (; ch + 8 <= nchunks; ch += 8) {   // independent loads in flight, then the running sum
+      int c[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) c[q] = chunk_counts[(int64_t)(ch + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        chunk_counts[(int64_t)(ch + q) * E + e] = run;
+        run += c[q];
+      }
+    }
+    for (; ch < nchunks; ++ch) {
+      const int cc = chunk_counts[(int64_t)ch * E + e];
       chunk_counts[(int64_t)ch * E + e] = run;
-      run += c;
+      run += cc;
     }
   }
   s_tot[e] = (e < E) ? run : 0;
   __syncthreads();
-  // exclusive scan over experts (Hillis-Steele on 256 entries)
-  for (int o = 1; o < 256; o <<= 1) {
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive scan over experts (Hillis-Steele)
     const int add = (e >= o) ? s_tot[e - o] : 0;
     __syncthreads();
     s_tot[e] += add;
@@ -150,6 +231,7 @@ __global__ void __launch_bounds__(256) scan_kernel(int32_t* __restrict__ chunk_c
   if (e == 0) offsets[0] = 0;
 }
 
+// Large plans, step 3: sorted position = offset + chunk base + rank in chunk.
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ ids, int64_t R, int E, int k,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ chunk_base,
@@ -157,10 +239,9 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
                                                       int32_t* __restrict__ sorted_rows,
                                                       int32_t* __restrict__ sorted_tokens,
                                                       int32_t* __restrict__ row_to_sorted) {
-  const int64_t chunk_rows = (int64_t)tokens_per_block(k) * k;
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R; r += (int64_t)gridDim.x * blockDim.x) {
     const int e = ids[r];
-    const int64_t ch = r / chunk_rows;
+    const int64_t ch = r / kChunkThreads;
     const int pos = offsets[e] + chunk_base[ch * E + e] + rank[r];
     sorted_rows[pos] = (int32_t)r;
     sorted_tokens[pos] = (int32_t)(r / k);
@@ -175,9 +256,9 @@ __global__ void zero_offsets_kernel(int32_t* offsets, int E) {
 }  // namespace
 
 size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k) {
-  const int64_t TB = tokens_per_block(k);
-  const int64_t nchunks = (T + TB - 1) / TB;
-  return (size_t)(nchunks * E + T * k) * sizeof(int32_t);
+  const int64_t R = T * k;
+  const int64_t nchunks = (R + kChunkThreads - 1) / kChunkThreads;
+  return (size_t)(nchunks * E + R) * sizeof(int32_t);
 }
 
 void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
@@ -187,14 +268,20 @@ void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t*
     hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, stream, offsets, E);
     return;
   }
-  const int64_t TB = tokens_per_block(k);
-  const int64_t nchunks = (T + TB - 1) / TB;
+  const int64_t R = T * k;
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), dim3(64 * kTopkWaves), 0,
+                     stream, logits, T, E, k, ids, weights);
+  if (R <= kSmallRows) {
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, ids, (int)R, E, k, offsets,
+                       sorted_rows, sorted_tokens, row_to_sorted);
+    return;
+  }
+  const int64_t nchunks = (R + kChunkThreads - 1) / kChunkThreads;
   int32_t* chunk_counts = static_cast<int32_t*>(ws);
   int32_t* rank = chunk_counts + nchunks * E;
-  hipLaunchKernelGGL(topk_rank_kernel, dim3((unsigned)nchunks), dim3(kRouteThreads), 0, stream, logits, T, E, k,
-                     ids, weights, chunk_counts, rank);
+  hipLaunchKernelGGL(rank_chunks_kernel, dim3((unsigned)nchunks), dim3(kChunkThreads), 0, stream, ids, R, E,
+                     chunk_counts, rank);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, stream, chunk_counts, (int)nchunks, E, offsets);
-  const int64_t R = T * k;
   int64_t blocks = (R + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ids, R, E, k, offsets,
