@@ -92,6 +92,24 @@ const char* w4a16_status_string(int status);
 /* Library ABI version (increments when a signature changes). */
 int w4a16_abi_version(void);
 
+/*
+ * GEMM kernel choice of w4a16_linear, w4a16_moe_gmm and w4a16_moe_layer.
+ *   W4_KERNEL_AUTO    (default) by the average rows per expert R/E: up to
+ *                     W4_TILED_MIN_ROWS the weight-streaming kernel (every
+ *                     weight byte read once per pass of 16 or 32 rows),
+ *                     above it the LDS-tiled MFMA kernel;
+ *   W4_KERNEL_STREAM  always the weight-streaming kernel;
+ *   W4_KERNEL_TILED   the tiled kernel wherever its shape conditions hold
+ *                     (gated: N/32 even; otherwise N % 64 == 0; E <= 256),
+ *                     else the streaming one.
+ * Both kernels compute the same products; their fp32 sums differ only in
+ * order.  Process-wide, not synchronised with launches in flight on other
+ * threads.  Returns the previous setting, or W4_ERR_ARG for an unknown value.
+ */
+enum { W4_KERNEL_AUTO = 0, W4_KERNEL_STREAM = 1, W4_KERNEL_TILED = 2 };
+#define W4_TILED_MIN_ROWS 64
+int w4a16_set_gemm_kernel(int kernel);
+
 /* Device-side group status values written by q4_group_repack. */
 #define W4_GROUP_OFF_GRID 0u    /* no m in 1..8 reproduced the group */
 #define W4_GROUP_NONFINITE 255u /* the group holds a NaN or an infinity */

@@ -24,6 +24,11 @@ W4_EPI_SWIGLU = 2
 W4_OUT_BF16 = 0
 W4_OUT_F32 = 1
 
+W4_KERNEL_AUTO = 0
+W4_KERNEL_STREAM = 1
+W4_KERNEL_TILED = 2
+W4_TILED_MIN_ROWS = 64
+
 W4_GROUP_OFF_GRID = 0
 W4_GROUP_NONFINITE = 255
 
@@ -36,6 +41,7 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "w4a16_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a16_abi_version": (ctypes.c_int, []),
+    "w4a16_set_gemm_kernel": (ctypes.c_int, [ctypes.c_int]),
     "q4_group_repack": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _p, _p]),
     "q4_group_dequant_f32": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
     "q4_pack_codes": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),

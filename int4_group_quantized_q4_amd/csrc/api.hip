@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "internal.h"
 #include "w4a16.h"
 
@@ -85,10 +87,22 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
   return launch_status();
 }
 
+static std::atomic<int> g_gemm_kernel{W4_KERNEL_AUTO};
+
+int w4a16_set_gemm_kernel(int kernel) {
+  if (kernel != W4_KERNEL_AUTO && kernel != W4_KERNEL_STREAM && kernel != W4_KERNEL_TILED) return W4_ERR_ARG;
+  return g_gemm_kernel.exchange(kernel);
+}
+
 static int run_gemm(const w4::GemmArgs& a, hipStream_t stream) {
   // Average rows per expert decides the kernel: weight-streaming (decode) or
   // LDS-tiled MFMA (prefill).
-  w4::launch_gemm_skinny(a, stream);
+  const int policy = g_gemm_kernel.load(std::memory_order_relaxed);
+  bool tiled = w4::gemm_tiled_supported(a);
+  if (policy == W4_KERNEL_STREAM) tiled = false;
+  else if (policy == W4_KERNEL_AUTO) tiled = tiled && a.R > (int64_t)W4_TILED_MIN_ROWS * a.E;
+  if (tiled) w4::launch_gemm_tiled(a, stream);
+  else w4::launch_gemm_skinny(a, stream);
   return launch_status();
 }
 

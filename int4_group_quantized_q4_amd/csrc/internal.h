@@ -30,6 +30,7 @@ struct GemmArgs {
 };
 
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+bool gemm_tiled_supported(const GemmArgs& a);
 void launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 
 size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);

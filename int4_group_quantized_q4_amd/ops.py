@@ -8,6 +8,7 @@ A few allocating helpers (``repack``, ``dequant``, ``pack_codes``,
 torch and then make the same calls.
 """
 
+import contextlib
 import ctypes
 
 import torch
@@ -71,6 +72,24 @@ def q4_pack_scales(scales, rows, K, scales_tiled, stream=None):
     st = lib().q4_pack_scales(_ptr(scales, "scales", _BF16_LIKE), rows, K,
                               _ptr(scales_tiled, "scales_tiled", _BF16_LIKE), _stream(stream))
     check(st, "q4_pack_scales")
+
+
+def w4a16_set_gemm_kernel(kernel):
+    """Process-wide GEMM kernel choice (W4_KERNEL_*); returns the previous one."""
+    prev = lib().w4a16_set_gemm_kernel(int(kernel))
+    if prev < 0:
+        check(prev, "w4a16_set_gemm_kernel")
+    return prev
+
+
+@contextlib.contextmanager
+def gemm_kernel(kernel):
+    """Run the enclosed calls with the given W4_KERNEL_* choice, then restore."""
+    prev = w4a16_set_gemm_kernel(kernel)
+    try:
+        yield
+    finally:
+        w4a16_set_gemm_kernel(prev)
 
 
 def w4a16_linear(x, qweight, scales, N, y, stream=None):

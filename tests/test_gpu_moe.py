@@ -154,5 +154,7 @@ def test_moe_layer_small_shapes():
     check_layer(cfg, "small")
 
 
-def test_moe_layer_prefill_full_size():
-    check_layer(gen.MOE_PREFILL, "moe-prefill")
+@pytest.mark.parametrize("kernel", [w4.W4_KERNEL_AUTO, w4.W4_KERNEL_STREAM])
+def test_moe_layer_prefill_full_size(kernel):
+    with w4.gemm_kernel(kernel):
+        check_layer(gen.MOE_PREFILL, "moe-prefill kernel=%d" % kernel)
