@@ -81,6 +81,8 @@ class MoeLayerSet:
         self.act = torch.empty(R, I, dtype=torch.bfloat16, device=device)
         self.o = torch.empty(R, d, dtype=torch.float32, device=device)
         self.y = torch.empty(T, d, dtype=torch.bfloat16, device=device)
+        gws = max(w4.w4a16_moe_gmm_workspace(T, R, E, d, 2 * I), w4.w4a16_moe_gmm_workspace(R, R, E, I, d))
+        self.gws = torch.empty(max(16, gws), dtype=torch.uint8, device=device)
 
     def step(self, c, ev=None):
         L = self.layers[c]
@@ -92,11 +94,11 @@ class MoeLayerSet:
         if ev is not None:
             ev[1].record()
         w4.w4a16_moe_gmm(L["x"], self.stoks, self.offs, E, R, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
-                         self.act, w4.W4_OUT_BF16)
+                         self.act, w4.W4_OUT_BF16, self.gws)
         if ev is not None:
             ev[2].record()
         w4.w4a16_moe_gmm(self.act, None, self.offs, E, R, I, d, L["w2q"], L["w2s"], w4.W4_EPI_NONE, self.o,
-                         w4.W4_OUT_F32)
+                         w4.W4_OUT_F32, self.gws)
         if ev is not None:
             ev[3].record()
         w4.w4a16_moe_combine(self.o, w4.W4_OUT_F32, self.r2s, self.wts, T, k, d, self.y)

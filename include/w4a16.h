@@ -102,8 +102,8 @@ int w4a16_abi_version(void);
  *   W4_KERNEL_TILED   the tiled kernel wherever its shape conditions hold
  *                     (gated: N/32 even; otherwise N % 64 == 0; E <= 256),
  *                     else the streaming one.
- * Both kernels compute the same products; their fp32 sums differ only in
- * order.  Process-wide, not synchronised with launches in flight on other
+ * Both kernels compute the same exact products; their fp32 sums differ only
+ * in order (see below).  Process-wide, not synchronised with launches in flight on other
  * threads.  Returns the previous setting, or W4_ERR_ARG for an unknown value.
  */
 enum { W4_KERNEL_AUTO = 0, W4_KERNEL_STREAM = 1, W4_KERNEL_TILED = 2 };
@@ -172,20 +172,40 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
                    hipStream_t stream);
 
 /*
+ * Products and accumulation of w4a16_linear and w4a16_moe_gmm.  Every product
+ * x * (s * q) is formed exactly and accumulated in fp32; only the order of the
+ * fp32 additions differs between the two kernels:
+ *   streaming kernel  bf16 MFMA on q, each 32-group's fp32 partial sum times
+ *                     its scale (decode shapes);
+ *   tiled kernel      fp16 MFMA on s*q, exact in fp16 for |s| in [2^-14, 2^13),
+ *                     with the activation rows converted to fp16 under a
+ *                     per-row power of two (exact for every value within 2^32
+ *                     of the row's largest magnitude; smaller ones round to
+ *                     fp16's finest step).  A block meeting a scale outside that
+ *                     range is recomputed by a second kernel with per-group
+ *                     fp32 scaling.
+ * The tiled kernel needs a workspace for the fp16 activation rows:
+ * w4a16_linear_workspace / w4a16_moe_gmm_workspace bytes, 16-byte aligned.  A
+ * call that selects the tiled kernel (w4a16_set_gemm_kernel) without enough
+ * workspace returns W4_ERR_WORKSPACE; the streaming kernel ignores ws.
+ */
+
+/*
  * w4a16_linear -- y = bf16(x . W^T), W[n][k] = s[n][k/32] * q[n][k].
  *
  * The W4A16 linear layer ([RQ] "What changed in vLLM's TPU backend"): int4
- * weights are dequantized on chip, activations stay bf16, products are exact
- * and accumulate in fp32 (each group's partial sum is scaled by its bf16 scale
- * in fp32), the output is rounded once to bf16.
+ * weights are dequantized on chip, products are exact and accumulate in fp32,
+ * the output is rounded once to bf16.
  *   x        in  [M][K] bf16
  *   qweight  in  N*K/2 bytes tile16; scales in N*K/32 bf16, tile16 scale layout
  *   y        out [M][N] bf16
+ *   ws       nullable workspace of ws_bytes (see above)
  * Requires N % 16 == 0, K % 32 == 0, M >= 0 (M == 0 enqueues nothing).
  */
+size_t w4a16_linear_workspace(int64_t M, int64_t K, int64_t N);
 int w4a16_linear(const uint16_t* x, int64_t M, int64_t K,
                  const uint8_t* qweight, const uint16_t* scales, int64_t N,
-                 uint16_t* y, hipStream_t stream);
+                 uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * w4a16_moe_route -- top-k routing plan of a mixture-of-experts layer.
@@ -228,14 +248,17 @@ int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
  *   expert_offsets in  [E+1] int32, non-decreasing, offsets[0] = 0, offsets[E] = R
  *   qweight        in  E * N*K/2 bytes (tile16 per expert); scales in E * N*K/32 (tile16 per expert)
  *   out            out [R][N] (EPI_NONE) or [R][N/2], of out_dtype
+ *   ws             nullable workspace of ws_bytes (see above)
  * Requires N % 16 == 0 (N % 32 == 0 with a gated epilogue), K % 32 == 0;
  * out_dtype must be W4_OUT_BF16 for gated epilogues.  Rows outside every
  * expert range are left untouched.
  */
+size_t w4a16_moe_gmm_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N);
 int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index,
                   const int32_t* expert_offsets, int32_t E, int64_t R, int64_t K, int64_t N,
                   const uint8_t* qweight, const uint16_t* scales,
-                  int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream);
+                  int32_t epilogue, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
 
 /*
  * w4a16_moe_combine -- y[t][n] = bf16( sum_{j<k} w[t][j] * o[row_to_sorted[t*k+j]][n] ),

@@ -46,10 +46,13 @@ SIGNATURES = {
     "q4_group_dequant_f32": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p]),
     "q4_pack_codes": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
     "q4_pack_scales": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
-    "w4a16_linear": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p]),
+    "w4a16_linear_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "w4a16_linear": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i64, _p, _p, ctypes.c_size_t, _p]),
     "w4a16_moe_route_workspace": (_sz, [_i64, _i32, _i32]),
     "w4a16_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
-    "w4a16_moe_gmm": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _i32, _p, _i32, _p]),
+    "w4a16_moe_gmm_workspace": (ctypes.c_size_t, [_i64, _i64, _i32, _i64, _i64]),
+    "w4a16_moe_gmm": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _i32, _p, _i32, _p,
+                                     ctypes.c_size_t, _p]),
     "w4a16_moe_combine": (ctypes.c_int, [_p, _i32, _p, _p, _i64, _i32, _i64, _p, _p]),
     "w4a16_moe_layer_workspace": (_sz, [_i64, _i32, _i32, _i64, _i64]),
     "w4a16_moe_layer_plan": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64, ctypes.POINTER(_sz)]),

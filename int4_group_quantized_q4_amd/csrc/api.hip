@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -94,20 +94,36 @@ int w4a16_set_gemm_kernel(int kernel) {
   return g_gemm_kernel.exchange(kernel);
 }
 
-static int run_gemm(const w4::GemmArgs& a, hipStream_t stream) {
+static int run_gemm(const w4::GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   // Average rows per expert decides the kernel: weight-streaming (decode) or
-  // LDS-tiled MFMA (prefill).
+  // LDS-tiled MFMA (prefill, needs the workspace for the fp16 activations).
   const int policy = g_gemm_kernel.load(std::memory_order_relaxed);
   bool tiled = w4::gemm_tiled_supported(a);
   if (policy == W4_KERNEL_STREAM) tiled = false;
   else if (policy == W4_KERNEL_AUTO) tiled = tiled && a.R > (int64_t)W4_TILED_MIN_ROWS * a.E;
-  if (tiled) w4::launch_gemm_tiled(a, stream);
-  else w4::launch_gemm_skinny(a, stream);
+  if (tiled) {
+    if (!ws || !aligned16(ws) || ws_bytes < w4::gemm_tiled_workspace(a.x_rows, a.R, a.E, a.K, a.N)) {
+      return W4_ERR_WORKSPACE;
+    }
+    w4::launch_gemm_tiled(a, ws, stream);
+  } else {
+    w4::launch_gemm_skinny(a, stream);
+  }
   return launch_status();
 }
 
+size_t w4a16_linear_workspace(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return 0;
+  return w4::gemm_tiled_workspace(M, M, 1, K, N);
+}
+
+size_t w4a16_moe_gmm_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N) {
+  if (x_rows < 0 || R < 0 || E < 1 || K < 0 || N < 0) return 0;
+  return w4::gemm_tiled_workspace(x_rows, R, E, K, N);
+}
+
 int w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight, const uint16_t* scales, int64_t N,
-                 uint16_t* y, hipStream_t stream) {
+                 uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M < 0) return W4_ERR_ARG;
   int st = check_matrix(N, K);
   if (st != W4_OK) return st;
@@ -118,6 +134,7 @@ int w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y)) return W4_ERR_ARG;
   w4::GemmArgs a{};
   a.x = x;
+  a.x_rows = M;
   a.row_index = nullptr;
   a.offsets = nullptr;
   a.E = 1;
@@ -129,7 +146,7 @@ int w4a16_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight
   a.epilogue = W4_EPI_NONE;
   a.out = y;
   a.out_dtype = W4_OUT_BF16;
-  return run_gemm(a, stream);
+  return run_gemm(a, ws, ws_bytes, stream);
 }
 
 size_t w4a16_moe_route_workspace(int64_t T, int32_t E, int32_t k) {
@@ -154,7 +171,8 @@ int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_
 
 int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, const int32_t* expert_offsets,
                   int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales,
-                  int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream) {
+                  int32_t epilogue, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
   if (x_rows < 0 || E < 1 || R < 0) return W4_ERR_ARG;
   if (epilogue != W4_EPI_NONE && epilogue != W4_EPI_GEGLU_TANH && epilogue != W4_EPI_SWIGLU) return W4_ERR_ARG;
   if (out_dtype != W4_OUT_BF16 && out_dtype != W4_OUT_F32) return W4_ERR_ARG;
@@ -170,6 +188,7 @@ int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, c
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(out)) return W4_ERR_ARG;
   w4::GemmArgs a{};
   a.x = x;
+  a.x_rows = x_rows;
   a.row_index = row_index;
   a.offsets = expert_offsets;
   a.E = E;
@@ -181,7 +200,7 @@ int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, c
   a.epilogue = epilogue;
   a.out = out;
   a.out_dtype = out_dtype;
-  return run_gemm(a, stream);
+  return run_gemm(a, ws, ws_bytes, stream);
 }
 
 int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sorted, const float* topk_weights,
@@ -211,11 +230,23 @@ int w4a16_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, 
   return W4_OK;
 }
 
+// The GEMM workspace (fp16 activations) follows the plan region; the two GEMMs
+// run one after the other and share it.
+static size_t layer_gemm_ws_offset(const size_t p[9], int64_t T, int32_t k, int64_t d) {
+  const size_t R = (size_t)T * (size_t)k;
+  return align256(p[8] + R * (size_t)d * 4);
+}
+
+static size_t layer_gemm_ws_bytes(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I) {
+  const size_t a = w4::gemm_tiled_workspace(T, T * (int64_t)k, E, d, 2 * I);
+  const size_t b = w4::gemm_tiled_workspace(T * (int64_t)k, T * (int64_t)k, E, I, d);
+  return a > b ? a : b;
+}
+
 size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I) {
   size_t p[9];
   if (w4a16_moe_layer_plan(T, E, k, d, I, p) != W4_OK) return 0;
-  const size_t R = (size_t)T * (size_t)k;
-  return align256(p[8] + R * (size_t)d * 4);
+  return layer_gemm_ws_offset(p, T, k, d) + layer_gemm_ws_bytes(T, E, k, d, I);
 }
 
 int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
@@ -241,12 +272,16 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
   void* rws = base + p[6];
   uint16_t* act = reinterpret_cast<uint16_t*>(base + p[7]);
   float* o = reinterpret_cast<float*>(base + p[8]);
+  void* gws = base + layer_gemm_ws_offset(p, T, k, d);
+  const size_t gws_bytes = layer_gemm_ws_bytes(T, E, k, d, I);
   const int64_t R = T * k;
   st = w4a16_moe_route(logits, T, E, k, ids, wts, offs, srows, stoks, r2s, rws, p[7] - p[6], stream);
   if (st != W4_OK) return st;
-  st = w4a16_moe_gmm(x, T, stoks, offs, E, R, d, 2 * I, w1_q, w1_s, activation, act, W4_OUT_BF16, stream);
+  st = w4a16_moe_gmm(x, T, stoks, offs, E, R, d, 2 * I, w1_q, w1_s, activation, act, W4_OUT_BF16, gws, gws_bytes,
+                     stream);
   if (st != W4_OK) return st;
-  st = w4a16_moe_gmm(act, R, nullptr, offs, E, R, I, d, w2_q, w2_s, W4_EPI_NONE, o, W4_OUT_F32, stream);
+  st = w4a16_moe_gmm(act, R, nullptr, offs, E, R, I, d, w2_q, w2_s, W4_EPI_NONE, o, W4_OUT_F32, gws, gws_bytes,
+                     stream);
   if (st != W4_OK) return st;
   return w4a16_moe_combine(o, W4_OUT_F32, r2s, wts, T, k, d, y, stream);
 }

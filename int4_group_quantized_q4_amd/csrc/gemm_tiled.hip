@@ -3,26 +3,41 @@
 // [RQ] "Repacked QAT Gemma 4 26B-A4B serves on one TPU v6e at 1.9x FP8
 // throughput", section "What changed in vLLM's TPU backend": the grouped
 // matmul takes a scale per 32-wide group and dequantizes each weight tile on
-// chip right before the multiply; activations stay bf16, accumulation fp32.
+// chip right before the multiply, with fp32 accumulation.
 //
-// Block tile: BM = 128 activation rows of one expert x 256 weight rows, K in
-// stages of 128 (one tile16 block = 4 groups).  4 waves, each owning all 128
-// rows x 64 weight rows (4 MFMA column tiles of 16).
-//  * Activations: the block's 128 gathered rows x 128 columns are staged in
-//    LDS, double-buffered through registers (rows past the expert's count
-//    re-read its first row; their results are never stored).
+// Number format.  A dequantized weight s*q (bf16 scale: 8 significant bits,
+// |q| <= 8: 3 more) needs 11 significant bits.  bf16 holds 8, fp16 holds 11, so
+// the weight tile is dequantized to fp16, where s*q is exact for every scale in
+// [2^-14, 2^13).  The activations enter as fp16 rows from rows_to_f16(): each
+// row was multiplied by a power of two 2^-e that puts its largest magnitude in
+// [2^14, 2^15), which converts every bf16 value exactly except magnitudes below
+// 2^-32 of the row's largest (rounded to fp16's 2^-24 quantum).  The fp16
+// MFMA's products are therefore the exact products of the bf16 operands (up to
+// that power of two), accumulated in fp32 straight in the MFMA accumulators;
+// the epilogue multiplies by 2^e.  A block whose scales leave the exact range
+// (zero, tiny, huge or non-finite) is recomputed by an exact path that scales
+// each group's fp32 partial sum instead.
+//
+// Block tile: BM = 128 activation rows of one expert x 256 weight rows (16
+// tile16 tiles), 4 waves each owning all 128 rows x 64 weight rows (4 MFMA
+// column tiles); two blocks per CU.  K advances in stages of 64 (2 groups).
+//  * Activations: a 4-stage ring of 16 KB LDS buffers filled by global->LDS DMA
+//    (each lane's 16 bytes go straight to LDS), three stages ahead.  Inside a
+//    buffer, row r's 16-byte chunk h sits at chunk h ^ ((r & 7) ^ ((r >> 3) & 1)),
+//    which keeps both the DMA writes and the MFMA operand reads free of bank
+//    conflicts.  Rows past the expert's count re-read its first row; their
+//    results are never stored.
 //  * Weights: each lane loads exactly its 16x16x32 MFMA B operand from the
-//    tile16 layout (one 16-byte load per column tile per stage, prefetched a
-//    stage ahead) and unpacks the codes in registers to exact bf16 q/16.
-//  * Per group: one MFMA per (row tile, column tile) into a zero accumulator,
-//    then acc += scale(row, group) * partial in fp32.  The exact weight is
-//    scale*q, which bf16 cannot hold, so the scale goes onto the fp32 partial
-//    sum; the epilogue multiplies by 16.
+//    tile16 layout (8 bytes per column tile per stage, one stage ahead) and
+//    expands it in registers: the offset-binary nibble u OR-ed into fp16 1024.0
+//    gives 1024 + u, minus 1032 gives q, times the fp16 scale gives s*q.
 // Gated epilogue: a wave's 4 column tiles are 2 gate tiles and the matching 2
 // up tiles, so act(gate) * up is formed in registers.
 // Scheduling: block b takes item (expert, row tile, column block) with the
 // column block fastest, dealt so that consecutive items share an XCD and its
 // L2: the row tile's activations and the expert's weights are re-read from L2.
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -32,14 +47,27 @@ namespace w4 {
 
 namespace {
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int BM = 128;                      // activation rows per block
 constexpr int WN_TILES = 4;                  // 16-row weight tiles per wave
 constexpr int NWAVES = 4;
 constexpr int BN_TILES = NWAVES * WN_TILES;  // weight tiles per block (256 rows)
 constexpr int MT = BM / 16;                  // MFMA row tiles per wave
-constexpr int XS = 128 * 2 + 16;             // LDS row stride of staged activations, bytes
-constexpr int ABUF = BM * XS;
-constexpr int APIECES = BM * 16 / (64 * NWAVES);  // 16-byte activation pieces per thread per stage
+constexpr int BK = 64;                       // K per stage: 2 groups
+constexpr int NST = 4;                       // LDS ring depth (activation stages)
+constexpr int AROW = BK * 2;                 // bytes of one staged activation row
+constexpr int ASTAGE = BM * AROW;            // 16 KB per stage
+constexpr int AQ = ASTAGE / (1024 * NWAVES); // DMA instructions per wave per stage
+
+// Exact-range test of bf16 scale pairs: |s| in [2^-14, 2^13) <=> the 15 low bits
+// minus 0x3880 (2^-14) stay below 0x0D80 (2^13 - 2^-14 in bf16 bit distance).
+constexpr unsigned kScaleLo = 0x3880u;
+// Fourth word of a raw buffer descriptor (32-bit data format, no swizzle).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr unsigned kScaleSpan = 0x0D80u;
 
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
@@ -47,6 +75,32 @@ __device__ __forceinline__ float gelu_tanh_f32(float x) {
 }
 
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ f32x4 mfma_f16(h8 a, h8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Chunk swizzle of a staged activation row (see the file comment).
+__device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory operations of this
+// wave still in flight, and every LDS access of this wave complete.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): waits are
+// explicit here.  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
 
 // Blocks are dispatched round-robin over the 8 XCDs; give XCD x a contiguous
 // range of items so neighbouring items share its L2.
@@ -111,10 +165,15 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
   return it;
 }
 
-template <int EPI, int OUT>
-__global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol_blocks) {
+// EXACT = false: the fast path; a block that meets a scale outside the exact
+// fp16 range stores nothing and sets redo[block].  EXACT = true (launched
+// next, same grid): only blocks with redo set run, recomputing their tile with
+// B = q in fp16 and each group's fp32 partial sum times its fp32 scale.
+template <int EPI, int OUT, bool EXACT>
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2)))
+tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
-  __shared__ __align__(16) uint8_t As[2 * ABUF];
+  __shared__ __align__(16) uint8_t As[NST * ASTAGE];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -124,6 +183,9 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
 
   const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, blockIdx.x);
   if (it.expert < 0) return;   // uniform over the block
+  if constexpr (EXACT) {
+    if (redo[blockIdx.x] == 0) return;
+  }
   const int e = __builtin_amdgcn_readfirstlane(it.expert);
   const int mt = __builtin_amdgcn_readfirstlane(it.mtile);
   const int nb = __builtin_amdgcn_readfirstlane(it.nblock);
@@ -157,51 +219,91 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
   }
 
   const int G = (int)(K / kGroup);
-  const int NBF = G / kBlockGroups;   // full 4-group blocks
+  const int NBF = G / kBlockGroups;        // full 4-group tile16 blocks
   const int gtail = G - NBF * kBlockGroups;
-  const uint8_t* wb[WN_TILES];
-  const uint16_t* sb[WN_TILES];
+  const int S = (G + 1) / 2;               // stages; the last holds one group when G is odd
+
+  // Operands are read through buffer descriptors: a uniform base and size in
+  // SGPRs, a 32-bit per-lane offset, a uniform per-tile offset; reads past the
+  // size return zeros instead of faulting.
+  const uint32_t wbytes = (uint32_t)(N * K / 2), sbytes = (uint32_t)(N * G * 2);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.qweight + (int64_t)e * (N * K / 2)), 0, wbytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t)e * N * G), 0, sbytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.xh, 0, (uint32_t)(a.x_rows * K * 2), kRsrcFlags);
+  uint32_t wtoff[WN_TILES], stoff[WN_TILES];   // uniform byte offsets of the tiles
 #pragma unroll
   for (int t = 0; t < WN_TILES; ++t) {
-    wb[t] = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)tile[t] * 8 * K;
-    sb[t] = a.scales + ((int64_t)e * N + (int64_t)tile[t] * kTileRows) * G;
+    wtoff[t] = (uint32_t)tile[t] * (uint32_t)(8 * K);
+    stoff[t] = (uint32_t)tile[t] * (uint32_t)(32 * G);
   }
 
-  // activation staging: piece p = thread + q*256 is row p/16, columns (p%16)*8 .. +8
-  const uint16_t* asrc[APIECES];
-  int adst[APIECES], acol[APIECES];
+  // ---- activation DMA: wave wv's instruction q fills bytes [1024n, 1024n+1024)
+  // of a stage buffer, n = AQ*wv + q: rows 8n .. 8n+7, lane -> row 8n + lane/8,
+  // chunk slot lane%8, which holds source chunk slot ^ aswz(row).
+  uint32_t aoff[AQ];   // byte offset of the lane's source chunk in stage 0
+  uint32_t ahigh = 0;  // bit q: that chunk lies in the second group of a stage
 #pragma unroll
-  for (int q = 0; q < APIECES; ++q) {
-    const int p = (int)threadIdx.x + q * 64 * NWAVES;
-    const int rr = p >> 4;
-    acol[q] = (p & 15) * 8;
+  for (int q = 0; q < AQ; ++q) {
+    const int n = AQ * wv + q;
+    const int rr = 8 * n + (lane >> 3);
+    const int ch = (lane & 7) ^ aswz(rr);
     const int64_t row = row_begin + (rr < cnt ? rr : 0);
     const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
-    asrc[q] = a.x + src * K;
-    adst[q] = rr * XS + acol[q] * 2;
+    aoff[q] = (uint32_t)(src * K * 2) + (uint32_t)(ch * 16);
+    ahigh |= (ch >= 4 ? 1u : 0u) << q;
   }
-  u32x4 ar[APIECES];
-  // columns at or past ncol re-read column 0 of the stage: they land in LDS
-  // columns that the partial last stage never reads
-  auto a_load = [&](int b, int ncol) __attribute__((always_inline)) {
+  auto a_issue = [&](int st) __attribute__((always_inline)) {
+    uint8_t* dst = As + (st % NST) * ASTAGE + (AQ * wv) * 1024;
+    // a one-group last stage re-reads chunks 0..3 in place of 4..7 (unused)
+    const bool one = 2 * st + 1 >= G;
 #pragma unroll
-    for (int q = 0; q < APIECES; ++q) {
-      const int col = acol[q] < ncol ? acol[q] : 0;
-      ar[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(asrc[q] + (int64_t)b * 128 + col));
+    for (int q = 0; q < AQ; ++q) {
+      const uint32_t voff = aoff[q] - ((one && ((ahigh >> q) & 1u)) ? 64u : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16,
+                                               voff, (uint32_t)st * AROW, 0, 0);
     }
   };
-  auto a_store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < APIECES; ++q) *reinterpret_cast<u32x4*>(As + buf * ABUF + adst[q]) = ar[q];
-  };
 
-  u32x4 bw[WN_TILES];
-  u32x2 bs[WN_TILES];
-  auto b_load = [&](int b) __attribute__((always_inline)) {
+  // ---- weights: per stage and tile, the two code words and two scales of the
+  // lane's row (tile16: block st/2, half st%2)
+  u32x2 bw[2][WN_TILES];
+  uint32_t bs[2][WN_TILES];
+  const uint32_t wlane = 16 * lane, slane = 8 * r;
+  // a stage inside a full tile16 block
+  auto b_issue_full = [&](int st, auto SLOT) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    const int blk = st >> 1, h = st & 1;
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) {
-      bw[t] = *reinterpret_cast<const u32x4*>(wb[t] + 1024 * (int64_t)b + 16 * lane);
-      bs[t] = *reinterpret_cast<const u32x2*>(sb[t] + 64 * (int64_t)b + 4 * r);
+      bw[sl][t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                rw, wlane + 8 * h, wtoff[t] + 1024 * blk, 0));
+      bs[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(rs, slane + 4 * h, stoff[t] + 128 * blk, 0);
+    }
+  };
+  auto b_issue = [&](int st, auto SLOT) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    const int blk = st >> 1, h = st & 1;
+    if (blk < NBF) {
+      b_issue_full(st, SLOT);
+    } else {
+      // partial last block of gtail groups: word stride 4*gtail per lane
+      const int j0 = 2 * h;
+      const bool two = j0 + 1 < gtail;
+      const int j1 = two ? j0 + 1 : j0;
+#pragma unroll
+      for (int t = 0; t < WN_TILES; ++t) {
+        const uint32_t wv0 = 4 * gtail * lane, sv0 = 2 * gtail * r;
+        const uint32_t so = wtoff[t] + 1024 * blk, ss = stoff[t] + 128 * blk;
+        bw[sl][t] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rw, wv0 + 4 * j0, so, 0),
+                          __builtin_amdgcn_raw_buffer_load_b32(rw, wv0 + 4 * j1, so, 0)};
+        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, sv0 + 2 * j0, ss, 0);
+        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rs, sv0 + 2 * j1, ss, 0);
+        // an absent second group gets scale 1.0 so the range test ignores it
+        bs[sl][t] = s0 | ((two ? s1 : 0x3F80u) << 16);
+      }
     }
   };
 
@@ -210,95 +312,158 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // one group j of a stage: B operands of the 4 tiles, their scales, 8 row tiles
-  auto group = [&](const uint8_t* Ab, int j, const uint32_t* words, const float* sc) __attribute__((always_inline)) {
-    bf16x8 B[WN_TILES];
+  // MFMA operand reads: row 16i + r, chunk 4j + c of the stage buffer
+  const int apos0 = (r * AROW) + ((c ^ aswz(r)) * 16);
+  const int apos1 = (r * AROW) + (((4 + c) ^ aswz(r)) * 16);
+  const h2 kOff = {(_Float16)1032.0f, (_Float16)1032.0f};
+
+  u16x2 srange = {0, 0};   // running max of (|scale bits| - kScaleLo), wrapping
+
+  // fast path: one group j of the current stage, B = s*q exactly in fp16
+  auto fast_group = [&](const uint8_t* Ab, int apos, auto CUR, int j) __attribute__((always_inline)) {
+    constexpr int cu = decltype(CUR)::value;
+    h8 B[WN_TILES];
 #pragma unroll
-    for (int t = 0; t < WN_TILES; ++t) B[t] = unpack8_div16(words[t]);
+    for (int t = 0; t < WN_TILES; ++t) {
+      const uint32_t w = bw[cu][t][j];
+      const uint32_t sbits = j ? (bs[cu][t] >> 16) : (bs[cu][t] & 0xFFFFu);
+      const _Float16 sh = (_Float16)bf16_to_f32(sbits);
+      const h2 s2 = {sh, sh};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t bits = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;
+        const h2 q2 = (__builtin_bit_cast(h2, bits) - kOff) * s2;
+        B[t][2 * d] = q2[0];
+        B[t][2 * d + 1] = q2[1];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(Ab + (16 * i + r) * XS + j * 64 + c * 16);
+      const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
-      for (int t = 0; t < WN_TILES; ++t) {
-        const f32x4 p = mfma16x16x32(A, B[t], zero4);
-        acc[i][t] += sc[t] * p;
-      }
-    }
-  };
-  auto full_stage = [&](int buf, const u32x4* cw, const u32x2* cs) __attribute__((always_inline)) {
-    const uint8_t* Ab = As + buf * ABUF;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t words[WN_TILES];
-      float sc[WN_TILES];
-#pragma unroll
-      for (int t = 0; t < WN_TILES; ++t) {
-        words[t] = cw[t][j];
-        const uint32_t pair = cs[t][j >> 1];
-        sc[t] = bf16_to_f32((j & 1) ? (pair >> 16) : (pair & 0xFFFFu));
-      }
-      group(Ab, j, words, sc);
+      for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A, B[t], acc[i][t]);
     }
   };
 
-  // prologue: stage 0
-  if (NBF > 0) {
-    a_load(0, 128);
-    b_load(0);
+  auto track_scales = [&](auto CUR) __attribute__((always_inline)) {
+    constexpr int cu = decltype(CUR)::value;
+#pragma unroll
+    for (int t = 0; t < WN_TILES; ++t) {
+      const u16x2 v = __builtin_bit_cast(u16x2, bs[cu][t] & 0x7FFF7FFFu) - u16x2{kScaleLo, kScaleLo};
+      srange = __builtin_elementwise_max(srange, v);
+    }
+  };
+
+  // Pipeline.  Issue order per stage s: B(s+1), then A(s+NST-1).  On entry to
+  // stage s, A(s) and B(s) have landed and every wave has passed the barrier
+  // after stage s-1, so buffer (s-1) % NST is free for A(s+NST-1).  At the end
+  // of stage s only A(s+NST-1), issued after B(s+1), may still be in flight.
+  //
+  // Steady stages: both groups present, B(s+1) in a full tile16 block, A(s+NST-1)
+  // exists -- no branches.
+  auto steady_stage = [&](int s, auto CUR) __attribute__((always_inline)) {
+    constexpr int cu = decltype(CUR)::value;
+    b_issue_full(s + 1, std::integral_constant<int, cu ^ 1>{});
+    a_issue(s + NST - 1);
+    const uint8_t* Ab = As + (s % NST) * ASTAGE;
+    track_scales(CUR);
+    fast_group(Ab, apos0, CUR, 0);
+    fast_group(Ab, apos1, CUR, 1);
+    wait_vm<AQ>();
+    barrier_only();
+  };
+  // Any stage (the last few): every condition checked.
+  auto generic_stage = [&](int s, auto CUR) __attribute__((always_inline)) {
+    constexpr int cu = decltype(CUR)::value;
+    const bool more = s + 1 < S;
+    const bool ahead = s + NST - 1 < S;
+    if (more) b_issue(s + 1, std::integral_constant<int, cu ^ 1>{});
+    if (ahead) a_issue(s + NST - 1);
+    const uint8_t* Ab = As + (s % NST) * ASTAGE;
+    track_scales(CUR);
+    fast_group(Ab, apos0, CUR, 0);
+    if (2 * s + 1 < G) fast_group(Ab, apos1, CUR, 1);
+    if (more) {
+      if (ahead) wait_vm<AQ>();
+      else wait_vm<0>();
+      barrier_only();
+    }
+  };
+
+  if constexpr (!EXACT) {
+    // prologue: B(0), then A(0) .. A(NST-2); wait for A(0) and B(0)
+    b_issue(0, std::integral_constant<int, 0>{});
+  #pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < S) a_issue(st);
+    if (S >= 3) wait_vm<2 * AQ>();
+    else if (S == 2) wait_vm<AQ>();
+    else wait_vm<0>();
+    barrier_only();
+
+    // stages [0, s_steady) are steady: s + NST - 1 < S and s + 1 < 2*NBF
+    const int s_steady = min(S - (NST - 1), 2 * NBF - 1);
+    int s = 0;
+  #pragma unroll 1
+    for (; s + 1 < s_steady; s += 2) {
+      steady_stage(s, std::integral_constant<int, 0>{});
+      steady_stage(s + 1, std::integral_constant<int, 1>{});
+    }
+    // at most NST stages remain (s is even here)
+    if (s < S) generic_stage(s, std::integral_constant<int, 0>{});
+    if (s + 1 < S) generic_stage(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < S) generic_stage(s + 2, std::integral_constant<int, 0>{});
+    if (s + 3 < S) generic_stage(s + 3, std::integral_constant<int, 1>{});
+
+    // Any scale outside the exact fp16 range anywhere in the block: leave the
+    // block to the exact kernel.
+    const bool bad = srange[0] >= kScaleSpan || srange[1] >= kScaleSpan;
+    const int anybad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) redo[blockIdx.x] = anybad ? 1 : 0;
+    if (anybad) return;
   } else {
-    a_load(0, gtail * kGroup);
-  }
-  a_store(0);
-  __syncthreads();
-
-  for (int s = 0; s + 1 < NBF; ++s) {
-    u32x4 cw[WN_TILES];
-    u32x2 cs[WN_TILES];
-#pragma unroll
-    for (int t = 0; t < WN_TILES; ++t) {
-      cw[t] = bw[t];
-      cs[t] = bs[t];
-    }
-    a_load(s + 1, 128);
-    b_load(s + 1);
-    full_stage(s & 1, cw, cs);
-    a_store((s + 1) & 1);
-    __syncthreads();
-  }
-  if (NBF > 0) {
-    u32x4 cw[WN_TILES];
-    u32x2 cs[WN_TILES];
-#pragma unroll
-    for (int t = 0; t < WN_TILES; ++t) {
-      cw[t] = bw[t];
-      cs[t] = bs[t];
-    }
-    if (gtail > 0) a_load(NBF, gtail * kGroup);
-    full_stage((NBF - 1) & 1, cw, cs);
-    if (gtail > 0) {
-      a_store(NBF & 1);
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
       __syncthreads();
-    }
-  }
-  if (gtail > 0) {
-    // the partial last block: gtail (1..3) groups, word stride 4*gtail per lane
-    const uint8_t* Ab = As + (NBF & 1) * ABUF;
-    for (int j = 0; j < gtail; ++j) {
-      uint32_t words[WN_TILES];
-      float sc[WN_TILES];
+      a_issue(s);   // into buffer s % NST
+      b_issue(s, std::integral_constant<int, 0>{});
+      wait_vm<0>();
+      __syncthreads();
+      const uint8_t* Ab = As + (s % NST) * ASTAGE;
+      const int ng = (2 * s + 1 < G) ? 2 : 1;
+      for (int j = 0; j < ng; ++j) {
+        h8 B[WN_TILES];
+        float sc[WN_TILES];
 #pragma unroll
-      for (int t = 0; t < WN_TILES; ++t) {
-        words[t] = *reinterpret_cast<const uint32_t*>(wb[t] + 1024 * (int64_t)NBF + 4 * gtail * lane + 4 * j);
-        sc[t] = bf16_to_f32(sb[t][64 * (int64_t)NBF + r * gtail + j]);
+        for (int t = 0; t < WN_TILES; ++t) {
+          const uint32_t w = bw[0][t][j];
+          sc[t] = bf16_to_f32(j ? (bs[0][t] >> 16) : (bs[0][t] & 0xFFFFu));
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t bits = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;
+            const h2 q2 = __builtin_bit_cast(h2, bits) - kOff;
+            B[t][2 * d] = q2[0];
+            B[t][2 * d + 1] = q2[1];
+          }
+        }
+        const int apos = j ? apos1 : apos0;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
+#pragma unroll
+          for (int t = 0; t < WN_TILES; ++t) {
+            const f32x4 p = mfma_f16(A, B[t], zero4);
+            acc[i][t] += sc[t] * p;
+          }
+        }
       }
-      group(Ab, j, words, sc);
     }
   }
 
   if (!active) return;
-  // D element q of row tile i: row 16i + 4*(lane/16) + q, weight row lane%16 of each tile
+  // D element q of row tile i: row 16i + 4*(lane/16) + q, weight row lane%16 of
+  // each tile; the row's activation exponent undoes the fp16 scaling.
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -306,11 +471,13 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
       const int rr = 16 * i + 4 * c + q;
       if (rr >= cnt) continue;
       const int64_t row = row_begin + rr;
+      const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
+      const int ex = a.xexp[src];
       if constexpr (GATED) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const float g = bf16_to_f32(f32_to_bf16(acc[i][t][q] * 16.0f));
-          const float u = bf16_to_f32(f32_to_bf16(acc[i][t + 2][q] * 16.0f));
+          const float g = bf16_to_f32(f32_to_bf16(ldexpf(acc[i][t][q], ex)));
+          const float u = bf16_to_f32(f32_to_bf16(ldexpf(acc[i][t + 2][q], ex)));
           const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
           static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)tile[t] * kTileRows + r] =
               (uint16_t)f32_to_bf16(act * u);
@@ -318,7 +485,7 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
       } else {
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t) {
-          const float v = acc[i][t][q] * 16.0f;
+          const float v = ldexpf(acc[i][t][q], ex);
           const int64_t o = row * N + (int64_t)tile[t] * kTileRows + r;
           if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[o] = v;
           else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16(v);
@@ -328,31 +495,104 @@ __global__ void __launch_bounds__(64 * NWAVES) tiled_kernel(GemmArgs a, int ncol
   }
 }
 
+// One wave per row: e = exponent putting max|x| in [2^14, 2^15), then
+// xh = fp16(x * 2^-e) (round to nearest even), xexp = e.
+__global__ void __launch_bounds__(256) rows_to_f16_kernel(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xh,
+                                                          int32_t* xexp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * K);
+  u32x4* dst = reinterpret_cast<u32x4*>(xh + row * K);
+  const int nch = (int)(K / 8);
+  uint32_t m = 0;
+  for (int ch = lane; ch < nch; ch += 64) {
+    const u32x4 v = src[ch];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, v[i] & 0x7FFFu);
+      m = max(m, (v[i] >> 16) & 0x7FFFu);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  int ex = 0;
+  if (m != 0 && m < 0x7F80u) {
+    int fe;
+    frexpf(bf16_to_f32(m), &fe);   // max|x| in [2^(fe-1), 2^fe)
+    ex = fe - 15;
+  }
+  for (int ch = lane; ch < nch; ch += 64) {
+    const u32x4 v = src[ch];
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(v[i] & 0xFFFFu), -ex);
+      const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(v[i] >> 16), -ex);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    dst[ch] = o;
+  }
+  if (lane == 0) xexp[row] = ex;
+}
+
 }  // namespace
 
 bool gemm_tiled_supported(const GemmArgs& a) {
   const int64_t tiles = a.N / kTileRows;
   if (a.E > 256 || a.R >= ((int64_t)1 << 31)) return false;
+  // activation byte offsets are 32-bit
+  if (a.x_rows * a.K * 2 >= ((int64_t)1 << 32)) return false;
   if (a.epilogue != W4_EPI_NONE) return (tiles / 2) % 2 == 0;   // gate tiles go in pairs
   return tiles % WN_TILES == 0;
 }
 
-void launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+static int64_t tiled_grid(const GemmArgs& a, int* ncol_blocks) {
   const bool gated = a.epilogue != W4_EPI_NONE;
   const int64_t tiles = a.N / kTileRows;
-  const int ncol_blocks = (int)(gated ? (tiles / 2 + BN_TILES / 2 - 1) / (BN_TILES / 2)
-                                      : (tiles + BN_TILES - 1) / BN_TILES);
+  *ncol_blocks = (int)(gated ? (tiles / 2 + BN_TILES / 2 - 1) / (BN_TILES / 2) : (tiles + BN_TILES - 1) / BN_TILES);
   // upper bound on the experts' row tiles: sum ceil(count/BM) <= R/BM + E
-  const int64_t mt_bound = a.R / BM + a.E;
-  const dim3 grid((unsigned)(mt_bound * ncol_blocks)), block(64 * NWAVES);
-  if (a.epilogue == W4_EPI_GEGLU_TANH)
-    hipLaunchKernelGGL((tiled_kernel<W4_EPI_GEGLU_TANH, W4_OUT_BF16>), grid, block, 0, stream, a, ncol_blocks);
-  else if (a.epilogue == W4_EPI_SWIGLU)
-    hipLaunchKernelGGL((tiled_kernel<W4_EPI_SWIGLU, W4_OUT_BF16>), grid, block, 0, stream, a, ncol_blocks);
-  else if (a.out_dtype == W4_OUT_F32)
-    hipLaunchKernelGGL((tiled_kernel<W4_EPI_NONE, W4_OUT_F32>), grid, block, 0, stream, a, ncol_blocks);
-  else
-    hipLaunchKernelGGL((tiled_kernel<W4_EPI_NONE, W4_OUT_BF16>), grid, block, 0, stream, a, ncol_blocks);
+  return (a.R / BM + a.E) * *ncol_blocks;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N) {
+  GemmArgs a{};
+  a.R = R;
+  a.E = E;
+  a.N = N;
+  a.epilogue = W4_EPI_NONE;   // the ungated grid is the larger one
+  int nc;
+  const int64_t blocks = tiled_grid(a, &nc);
+  return align256((size_t)x_rows * (size_t)K * 2) + align256((size_t)x_rows * 4) + align256((size_t)blocks);
+}
+
+template <int EPI, int OUT>
+static void launch_pair(const GemmArgs& a, int64_t blocks, int ncol_blocks, uint8_t* redo, hipStream_t stream) {
+  const dim3 grid((unsigned)blocks), block(64 * NWAVES);
+  hipLaunchKernelGGL((tiled_kernel<EPI, OUT, false>), grid, block, 0, stream, a, ncol_blocks, redo);
+  hipLaunchKernelGGL((tiled_kernel<EPI, OUT, true>), grid, block, 0, stream, a, ncol_blocks, redo);
+}
+
+void launch_gemm_tiled(const GemmArgs& a_in, void* ws, hipStream_t stream) {
+  GemmArgs a = a_in;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t xh_bytes = align256((size_t)a.x_rows * (size_t)a.K * 2);
+  const size_t xe_bytes = align256((size_t)a.x_rows * 4);
+  a.xh = reinterpret_cast<uint16_t*>(base);
+  a.xexp = reinterpret_cast<int32_t*>(base + xh_bytes);
+  uint8_t* redo = base + xh_bytes + xe_bytes;
+  if (a.x_rows > 0) {
+    hipLaunchKernelGGL(rows_to_f16_kernel, dim3((unsigned)((a.x_rows + 3) / 4)), dim3(256), 0, stream, a.x, a.x_rows,
+                       a.K, const_cast<uint16_t*>(a.xh), const_cast<int32_t*>(a.xexp));
+  }
+  int nc;
+  const int64_t blocks = tiled_grid(a, &nc);
+  if (a.epilogue == W4_EPI_GEGLU_TANH) launch_pair<W4_EPI_GEGLU_TANH, W4_OUT_BF16>(a, blocks, nc, redo, stream);
+  else if (a.epilogue == W4_EPI_SWIGLU) launch_pair<W4_EPI_SWIGLU, W4_OUT_BF16>(a, blocks, nc, redo, stream);
+  else if (a.out_dtype == W4_OUT_F32) launch_pair<W4_EPI_NONE, W4_OUT_F32>(a, blocks, nc, redo, stream);
+  else launch_pair<W4_EPI_NONE, W4_OUT_BF16>(a, blocks, nc, redo, stream);
 }
 
 }  // namespace w4

@@ -17,6 +17,7 @@ void launch_pack_scales(const uint16_t* src, int64_t rows, int64_t K, uint16_t* 
 // Grouped W4A16 matmul arguments (a dense linear layer is E = 1, no offsets).
 struct GemmArgs {
   const uint16_t* x;         // [x_rows][K] bf16
+  int64_t x_rows;
   const int32_t* row_index;  // nullable, [R]
   const int32_t* offsets;    // nullable (dense: rows [0, R) belong to expert 0), [E+1]
   int32_t E;
@@ -27,11 +28,15 @@ struct GemmArgs {
   int32_t epilogue;          // W4_EPI_*
   void* out;
   int32_t out_dtype;         // W4_OUT_*
+  // set by launch_gemm_tiled: x as fp16 rows scaled by 2^-xexp[row]
+  const uint16_t* xh;
+  const int32_t* xexp;
 };
 
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 bool gemm_tiled_supported(const GemmArgs& a);
-void launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N);
+void launch_gemm_tiled(const GemmArgs& a, void* ws, hipStream_t stream);
 
 size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);
 void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,

@@ -92,10 +92,19 @@ def gemm_kernel(kernel):
         w4a16_set_gemm_kernel(prev)
 
 
-def w4a16_linear(x, qweight, scales, N, y, stream=None):
+def _ws(ws):
+    return (_ptr(ws, "ws", None, True), 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def w4a16_linear_workspace(M, K, N):
+    return int(lib().w4a16_linear_workspace(M, K, N))
+
+
+def w4a16_linear(x, qweight, scales, N, y, ws=None, stream=None):
     M, K = x.shape
+    wp, wn = _ws(ws)
     st = lib().w4a16_linear(_ptr(x, "x", _BF16_LIKE), M, K, _ptr(qweight, "qweight", (torch.uint8,)),
-                            _ptr(scales, "scales", _BF16_LIKE), N, _ptr(y, "y", _BF16_LIKE), _stream(stream))
+                            _ptr(scales, "scales", _BF16_LIKE), N, _ptr(y, "y", _BF16_LIKE), wp, wn, _stream(stream))
     check(st, "w4a16_linear")
 
 
@@ -116,14 +125,25 @@ def w4a16_moe_route(logits, k, topk_ids, topk_weights, expert_offsets, sorted_ro
     check(st, "w4a16_moe_route")
 
 
+def w4a16_moe_gmm_workspace(x_rows, R, E, K, N):
+    return int(lib().w4a16_moe_gmm_workspace(x_rows, R, E, K, N))
+
+
 def w4a16_moe_gmm(x, row_index, expert_offsets, E, R, K, N, qweight, scales, epilogue, out, out_dtype,
-                  stream=None):
+                  ws=None, stream=None):
+    wp, wn = _ws(ws)
     st = lib().w4a16_moe_gmm(
         _ptr(x, "x", _BF16_LIKE), x.shape[0], _ptr(row_index, "row_index", (torch.int32,), True),
         _ptr(expert_offsets, "expert_offsets", (torch.int32,)), E, R, K, N,
         _ptr(qweight, "qweight", (torch.uint8,)), _ptr(scales, "scales", _BF16_LIKE), epilogue,
-        _ptr(out, "out", (torch.float32,) + _BF16_LIKE), out_dtype, _stream(stream))
+        _ptr(out, "out", (torch.float32,) + _BF16_LIKE), out_dtype, wp, wn, _stream(stream))
     check(st, "w4a16_moe_gmm")
+
+
+def moe_gmm(x, row_index, expert_offsets, E, R, K, N, qweight, scales, epilogue, out, out_dtype, stream=None):
+    """w4a16_moe_gmm with a freshly allocated workspace."""
+    ws = torch.empty(max(16, w4a16_moe_gmm_workspace(x.shape[0], R, E, K, N)), dtype=torch.uint8, device=x.device)
+    w4a16_moe_gmm(x, row_index, expert_offsets, E, R, K, N, qweight, scales, epilogue, out, out_dtype, ws, stream)
 
 
 def w4a16_moe_combine(o, o_dtype, row_to_sorted, topk_weights, T, k, N, y, stream=None):
@@ -190,8 +210,10 @@ def pack_scales(scales, stream=None):
 
 
 def linear(x, qweight, scales, N, stream=None):
-    y = torch.empty(x.shape[0], N, dtype=torch.bfloat16, device=x.device)
-    w4a16_linear(x, qweight, scales, N, y, stream)
+    M, K = x.shape
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    ws = torch.empty(max(16, w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=x.device)
+    w4a16_linear(x, qweight, scales, N, y, ws, stream)
     return y
 
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.w4a16_abi_version() == 1
+    assert lib.w4a16_abi_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert len(w4.status_string(st)) > 5
     assert "unknown" in w4.status_string(42)
@@ -63,13 +63,14 @@ def test_repack_argument_errors():
 
 def test_linear_and_gmm_argument_errors():
     lib = _lib.lib()
-    assert lib.w4a16_linear(FAKE, 4, 256, FAKE, FAKE, 500, FAKE, None) == w4.W4_ERR_SHAPE
-    assert lib.w4a16_linear(FAKE, 4, 250, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_SHAPE
-    assert lib.w4a16_linear(FAKE, -1, 256, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_ARG
-    assert lib.w4a16_linear(None, 4, 256, FAKE, FAKE, 512, FAKE, None) == w4.W4_ERR_ARG
-    assert lib.w4a16_linear(FAKE, 0, 256, None, None, 512, None, None) == w4.W4_OK
+    assert lib.w4a16_linear(FAKE, 4, 256, FAKE, FAKE, 500, FAKE, None, 0, None) == w4.W4_ERR_SHAPE
+    assert lib.w4a16_linear(FAKE, 4, 250, FAKE, FAKE, 512, FAKE, None, 0, None) == w4.W4_ERR_SHAPE
+    assert lib.w4a16_linear(FAKE, -1, 256, FAKE, FAKE, 512, FAKE, None, 0, None) == w4.W4_ERR_ARG
+    assert lib.w4a16_linear(None, 4, 256, FAKE, FAKE, 512, FAKE, None, 0, None) == w4.W4_ERR_ARG
+    assert lib.w4a16_linear(FAKE, 0, 256, None, None, 512, None, None, 0, None) == w4.W4_OK
     g = lib.w4a16_moe_gmm
-    args = [FAKE, 64, FAKE, FAKE, 128, 512, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16, None]
+    args = [FAKE, 64, FAKE, FAKE, 128, 512, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16, None, 0,
+            None]
     bad = list(args); bad[10] = 7
     assert g(*bad) == w4.W4_ERR_ARG
     bad = list(args); bad[12] = w4.W4_OUT_F32               # gated epilogue needs bf16 out
@@ -82,6 +83,23 @@ def test_linear_and_gmm_argument_errors():
     assert g(*bad) == w4.W4_ERR_ARG
     bad = list(args); bad[4] = 0
     assert g(*bad) == w4.W4_ERR_ARG
+
+
+def test_tiled_kernel_needs_workspace():
+    """A prefill-shaped call (many rows per expert) selects the tiled kernel,
+    whose fp16 activation rows live in the caller's workspace: without it the
+    call fails on the host, before any launch."""
+    lib = _lib.lib()
+    need = lib.w4a16_moe_gmm_workspace(4096, 32768, 128, 2816, 1408)
+    assert need >= 4096 * 2816 * 2 + 4096 * 4 and need % 256 == 0
+    assert lib.w4a16_linear_workspace(300, 2816, 512) >= 300 * 2816 * 2
+    args = [FAKE, 4096, FAKE, FAKE, 128, 32768, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16,
+            None, 0, None]
+    assert lib.w4a16_moe_gmm(*args) == w4.W4_ERR_WORKSPACE
+    args[13], args[14] = FAKE, need - 1
+    assert lib.w4a16_moe_gmm(*args) == w4.W4_ERR_WORKSPACE
+    with w4.gemm_kernel(w4.W4_KERNEL_TILED):
+        assert lib.w4a16_linear(FAKE, 300, 2816, FAKE, FAKE, 512, FAKE, None, 0, None) == w4.W4_ERR_WORKSPACE
 
 
 def test_route_combine_layer_argument_errors():

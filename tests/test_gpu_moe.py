@@ -80,7 +80,7 @@ def test_gmm_plain_f32_with_gather(E, R, K, N):
     offsets, R, x, row_index, packed, sct, codes, sc = _gmm_case(E, R, K, N, E + R + K + N)
     say("[gmm] E=%d R=%d K=%d N=%d" % (E, R, K, N))
     out = torch.full((R, N), float("nan"), dtype=torch.float32, device="cuda")
-    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
+    w4.moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
                      w4.W4_EPI_NONE, out, w4.W4_OUT_F32)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
@@ -100,7 +100,7 @@ def test_gmm_gated_epilogue(act):
     offsets, R, x, row_index, packed, sct, codes, sc = _gmm_case(E, R, K, N, 77 + act)
     say("[gmm gated] act=%d" % act)
     out = torch.empty((R, N // 2), dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
+    w4.moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
                      act, out, w4.W4_OUT_BF16)
     torch.cuda.synchronize()
     got = oracle.bf16_bits_to_f64(bits_host(out))

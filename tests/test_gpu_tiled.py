@@ -37,7 +37,7 @@ def run_gmm(kernel, offsets, R, x, row_index, packed, sct, E, K, N, epi, out_dty
     tdt = torch.float32 if out_dtype == w4.W4_OUT_F32 else torch.bfloat16
     out = torch.full((R, cols), float("nan"), dtype=tdt, device="cuda")
     with w4.gemm_kernel(kernel):
-        w4.w4a16_moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed),
+        w4.moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed),
                          bf16_dev(sct), epi, out, out_dtype)
     torch.cuda.synchronize()
     if out_dtype == w4.W4_OUT_F32:
