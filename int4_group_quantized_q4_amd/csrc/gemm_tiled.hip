@@ -53,11 +53,17 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;                      // activation rows per block
 constexpr int WN_TILES = 4;                  // 16-row weight tiles per wave
-constexpr int NWAVES = 4;
-constexpr int BN_TILES = NWAVES * WN_TILES;  // weight tiles per block (256 rows)
+#ifndef W4_TILED_WAVES
+#define W4_TILED_WAVES 4
+#endif
+#ifndef W4_TILED_NST
+#define W4_TILED_NST 4
+#endif
+constexpr int NWAVES = W4_TILED_WAVES;       // 2 per SIMD
+constexpr int BN_TILES = NWAVES * WN_TILES;  // weight tiles per block
 constexpr int MT = BM / 16;                  // MFMA row tiles per wave
 constexpr int BK = 64;                       // K per stage: 2 groups
-constexpr int NST = 4;                       // LDS ring depth (activation stages)
+constexpr int NST = W4_TILED_NST;            // LDS ring depth (activation stages)
 constexpr int AROW = BK * 2;                 // bytes of one staged activation row
 constexpr int ASTAGE = BM * AROW;            // 16 KB per stage
 constexpr int AQ = ASTAGE / (1024 * NWAVES); // DMA instructions per wave per stage
@@ -69,15 +75,32 @@ constexpr unsigned kScaleLo = 0x3880u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr unsigned kScaleSpan = 0x0D80u;
 
+// gelu with the tanh approximation, tanh(y) = 1 - 2 / (1 + e^(2y)): the
+// absolute error of the hardware exp and reciprocal (~1e-7) moves
+// 0.5 x (1 + tanh) by ~1e-7 relative, far below the bf16 rounding that follows.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+  const float y = c * (x + 0.044715f * x * x * x);
+  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * y));
+  return 0.5f * x * (1.0f + th);
 }
 
-__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ f32x4 mfma_f16(h8 a, h8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// fp16 pairs 1024 + u of a tile16 word's codes (2d, 2d+1), d = 0..3: the low
+// nibbles of the word's bytes are codes 0, 4, 1, 5 and the high nibbles codes
+// 2, 6, 3, 7; a byte permute places each code below the fp16 exponent byte 0x64.
+__device__ __forceinline__ void biased_f16_pairs(uint32_t w, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  out[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04020400u);
+  out[1] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04020400u);
+  out[2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030401u);
+  out[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030401u);
 }
 
 // Chunk swizzle of a staged activation row (see the file comment).
@@ -170,7 +193,10 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
 // next, same grid): only blocks with redo set run, recomputing their tile with
 // B = q in fp16 and each group's fp32 partial sum times its fp32 scale.
 template <int EPI, int OUT, bool EXACT>
-__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2)))
+#ifndef W4_TILED_WPE
+#define W4_TILED_WPE 2
+#endif
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(W4_TILED_WPE)))
 tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   __shared__ __align__(16) uint8_t As[NST * ASTAGE];
@@ -181,11 +207,12 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   const int c = lane >> 4;
   const int64_t K = a.K, N = a.N;
 
-  const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, blockIdx.x);
-  if (it.expert < 0) return;   // uniform over the block
+  // (redo[] is valid only for blocks that hold an item; find_item decides)
   if constexpr (EXACT) {
     if (redo[blockIdx.x] == 0) return;
   }
+  const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, blockIdx.x);
+  if (it.expert < 0) return;   // uniform over the block
   const int e = __builtin_amdgcn_readfirstlane(it.expert);
   const int mt = __builtin_amdgcn_readfirstlane(it.mtile);
   const int nb = __builtin_amdgcn_readfirstlane(it.nblock);
@@ -255,8 +282,9 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     aoff[q] = (uint32_t)(src * K * 2) + (uint32_t)(ch * 16);
     ahigh |= (ch >= 4 ? 1u : 0u) << q;
   }
-  auto a_issue = [&](int st) __attribute__((always_inline)) {
-    uint8_t* dst = As + (st % NST) * ASTAGE + (AQ * wv) * 1024;
+  // activations of stage `st` into the buffer of stage `slot_st`
+  auto a_issue = [&](int st, int slot_st) __attribute__((always_inline)) {
+    uint8_t* dst = As + (slot_st % NST) * ASTAGE + (AQ * wv) * 1024;
     // a one-group last stage re-reads chunks 0..3 in place of 4..7 (unused)
     const bool one = 2 * st + 1 >= G;
 #pragma unroll
@@ -267,43 +295,28 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     }
   };
 
-  // ---- weights: per stage and tile, the two code words and two scales of the
-  // lane's row (tile16: block st/2, half st%2)
-  u32x2 bw[2][WN_TILES];
-  uint32_t bs[2][WN_TILES];
-  const uint32_t wlane = 16 * lane, slane = 8 * r;
-  // a stage inside a full tile16 block
-  auto b_issue_full = [&](int st, auto SLOT) __attribute__((always_inline)) {
+  // ---- weights: per tile16 block b (stages 2b and 2b+1) and tile, the lane's
+  // four code words (groups 0..3) and four scales.  A full block holds them at
+  // 16*lane and 8*r bytes; the partial last block (gtail groups) at
+  // 4*gtail*lane and 2*gtail*r, where the same 16- and 8-byte loads pick up
+  // words 0..gtail-1 (the rest is the next rows' data or, past the end of the
+  // buffer, zeros -- never used).
+  const int NB = NBF + (gtail > 0 ? 1 : 0);
+  u32x4 bw[2][WN_TILES];
+  u32x2 bs[2][WN_TILES];
+  auto bblk_issue = [&](int blk, auto SLOT) __attribute__((always_inline)) {
     constexpr int sl = decltype(SLOT)::value;
-    const int blk = st >> 1, h = st & 1;
+    const bool tail = blk >= NBF;
+    const uint32_t wv = tail ? (uint32_t)(4 * gtail * lane) : (uint32_t)(16 * lane);
+    // scale rows of a partial block start at 2-byte boundaries: load from the
+    // dword below and shift the row's first scale down to bit 0
+    const uint32_t sv = tail ? (uint32_t)(2 * gtail * r) : (uint32_t)(8 * r);
+    const uint32_t sva = sv & ~3u, ssh = (sv & 3u) * 8u;
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) {
-      bw[sl][t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rw, wlane + 8 * h, wtoff[t] + 1024 * blk, 0));
-      bs[sl][t] = __builtin_amdgcn_raw_buffer_load_b32(rs, slane + 4 * h, stoff[t] + 128 * blk, 0);
-    }
-  };
-  auto b_issue = [&](int st, auto SLOT) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SLOT)::value;
-    const int blk = st >> 1, h = st & 1;
-    if (blk < NBF) {
-      b_issue_full(st, SLOT);
-    } else {
-      // partial last block of gtail groups: word stride 4*gtail per lane
-      const int j0 = 2 * h;
-      const bool two = j0 + 1 < gtail;
-      const int j1 = two ? j0 + 1 : j0;
-#pragma unroll
-      for (int t = 0; t < WN_TILES; ++t) {
-        const uint32_t wv0 = 4 * gtail * lane, sv0 = 2 * gtail * r;
-        const uint32_t so = wtoff[t] + 1024 * blk, ss = stoff[t] + 128 * blk;
-        bw[sl][t] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rw, wv0 + 4 * j0, so, 0),
-                          __builtin_amdgcn_raw_buffer_load_b32(rw, wv0 + 4 * j1, so, 0)};
-        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rs, sv0 + 2 * j0, ss, 0);
-        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rs, sv0 + 2 * j1, ss, 0);
-        // an absent second group gets scale 1.0 so the range test ignores it
-        bs[sl][t] = s0 | ((two ? s1 : 0x3F80u) << 16);
-      }
+      bw[sl][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv, wtoff[t] + 1024 * blk, 0));
+      const uint64_t sc64 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, sva, stoff[t] + 128 * blk, 0));
+      bs[sl][t] = __builtin_bit_cast(u32x2, sc64 >> ssh);
     }
   };
 
@@ -320,20 +333,41 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
 
   u16x2 srange = {0, 0};   // running max of (|scale bits| - kScaleLo), wrapping
 
-  // fast path: one group j of the current stage, B = s*q exactly in fp16
-  auto fast_group = [&](const uint8_t* Ab, int apos, auto CUR, int j) __attribute__((always_inline)) {
-    constexpr int cu = decltype(CUR)::value;
+  // The block's scales as fp16 pairs (groups 0,1 and 2,3), converted once per
+  // block; exact for every scale in the fast path's range.
+  h2 sfh[WN_TILES][2];
+  auto block_scales = [&](int blk, auto SLOT) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    const int ngb = blk < NBF ? kBlockGroups : gtail;   // groups present
+#pragma unroll
+    for (int t = 0; t < WN_TILES; ++t) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t w = bs[sl][t][p];
+        sfh[t][p] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16)));
+        // range test; an absent group counts as scale 1.0
+        const uint32_t lo = (2 * p < ngb) ? (w & 0xFFFFu) : 0x3F80u;
+        const uint32_t hi = (2 * p + 1 < ngb) ? (w >> 16) : 0x3F80u;
+        const u16x2 v = __builtin_bit_cast(u16x2, (lo | (hi << 16)) & 0x7FFF7FFFu) - u16x2{kScaleLo, kScaleLo};
+        srange = __builtin_elementwise_max(srange, v);
+      }
+    }
+  };
+
+  // fast path: group g (0..3) of the block in slot SLOT, B = s*q exactly in fp16
+  auto fast_group = [&](const uint8_t* Ab, int apos, auto SLOT, auto GRP) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr int g = decltype(GRP)::value;
     h8 B[WN_TILES];
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) {
-      const uint32_t w = bw[cu][t][j];
-      const uint32_t sbits = j ? (bs[cu][t] >> 16) : (bs[cu][t] & 0xFFFFu);
-      const _Float16 sh = (_Float16)bf16_to_f32(sbits);
+      uint32_t pr[4];
+      biased_f16_pairs(bw[sl][t][g], pr);
+      const _Float16 sh = sfh[t][g >> 1][g & 1];
       const h2 s2 = {sh, sh};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t bits = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;
-        const h2 q2 = (__builtin_bit_cast(h2, bits) - kOff) * s2;
+        const h2 q2 = (__builtin_bit_cast(h2, pr[d]) - kOff) * s2;
         B[t][2 * d] = q2[0];
         B[t][2 * d + 1] = q2[1];
       }
@@ -346,75 +380,60 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     }
   };
 
-  auto track_scales = [&](auto CUR) __attribute__((always_inline)) {
-    constexpr int cu = decltype(CUR)::value;
-#pragma unroll
-    for (int t = 0; t < WN_TILES; ++t) {
-      const u16x2 v = __builtin_bit_cast(u16x2, bs[cu][t] & 0x7FFF7FFFu) - u16x2{kScaleLo, kScaleLo};
-      srange = __builtin_elementwise_max(srange, v);
-    }
-  };
-
-  // Pipeline.  Issue order per stage s: B(s+1), then A(s+NST-1).  On entry to
-  // stage s, A(s) and B(s) have landed and every wave has passed the barrier
-  // after stage s-1, so buffer (s-1) % NST is free for A(s+NST-1).  At the end
-  // of stage s only A(s+NST-1), issued after B(s+1), may still be in flight.
-  //
-  // Steady stages: both groups present, B(s+1) in a full tile16 block, A(s+NST-1)
-  // exists -- no branches.
-  auto steady_stage = [&](int s, auto CUR) __attribute__((always_inline)) {
-    constexpr int cu = decltype(CUR)::value;
-    b_issue_full(s + 1, std::integral_constant<int, cu ^ 1>{});
-    a_issue(s + NST - 1);
+  // Pipeline.  Stage s computes groups 2h, 2h+1 (h = s % 2) of tile16 block
+  // s/2 from LDS buffer s % NST.  Issue order: an even stage issues the next
+  // block's weights, then every stage the activations of stage s + NST - 1;
+  // issues past the end re-read the last block/stage into a free slot, so the
+  // number of loads in flight is the same at every stage and the waits are
+  // fixed:
+  //   end of an even stage: A(s+1) has landed -- after it come A(s+2) ..
+  //     A(s+NST-1) and (at most) one block's 8 weight loads;
+  //   end of an odd stage: A(s+1) and the next block have landed -- after the
+  //     block come A(s+NST-2) and A(s+NST-1).
+  // The barrier then makes every wave's DMA visible and frees buffer s % NST,
+  // which the next stage's DMA refills.
+  const int last_st = S - 1;
+  auto stage = [&](int s, auto SLOT, auto HALF) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    constexpr int h = decltype(HALF)::value;
+    const int nb = (s >> 1) + 1;
+    const int nbc = nb < NB ? nb : NB - 1;
+    if constexpr (h == 0) bblk_issue(nbc, std::integral_constant<int, sl ^ 1>{});
+    a_issue(s + NST - 1 <= last_st ? s + NST - 1 : last_st, s + NST - 1);
+    // keep the loads at the top of the stage: sunk to its end they would be
+    // waited for at once
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* Ab = As + (s % NST) * ASTAGE;
-    track_scales(CUR);
-    fast_group(Ab, apos0, CUR, 0);
-    fast_group(Ab, apos1, CUR, 1);
-    wait_vm<AQ>();
+    if constexpr (h == 0) block_scales(s >> 1, SLOT);
+    fast_group(Ab, apos0, SLOT, std::integral_constant<int, 2 * h>{});
+    if (2 * s + 1 < G) fast_group(Ab, apos1, SLOT, std::integral_constant<int, 2 * h + 1>{});
+    if constexpr (h == 0) wait_vm<(NST - 2) * AQ + 2 * WN_TILES>();
+    else wait_vm<2 * AQ>();
     barrier_only();
-  };
-  // Any stage (the last few): every condition checked.
-  auto generic_stage = [&](int s, auto CUR) __attribute__((always_inline)) {
-    constexpr int cu = decltype(CUR)::value;
-    const bool more = s + 1 < S;
-    const bool ahead = s + NST - 1 < S;
-    if (more) b_issue(s + 1, std::integral_constant<int, cu ^ 1>{});
-    if (ahead) a_issue(s + NST - 1);
-    const uint8_t* Ab = As + (s % NST) * ASTAGE;
-    track_scales(CUR);
-    fast_group(Ab, apos0, CUR, 0);
-    if (2 * s + 1 < G) fast_group(Ab, apos1, CUR, 1);
-    if (more) {
-      if (ahead) wait_vm<AQ>();
-      else wait_vm<0>();
-      barrier_only();
-    }
   };
 
   if constexpr (!EXACT) {
-    // prologue: B(0), then A(0) .. A(NST-2); wait for A(0) and B(0)
-    b_issue(0, std::integral_constant<int, 0>{});
-  #pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-      if (st < S) a_issue(st);
-    if (S >= 3) wait_vm<2 * AQ>();
-    else if (S == 2) wait_vm<AQ>();
-    else wait_vm<0>();
+    // prologue: block 0, then A(0) .. A(NST-2); wait for A(0) and block 0
+    bblk_issue(0, std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) a_issue(st <= last_st ? st : last_st, st);
+    wait_vm<(NST - 2) * AQ>();
     barrier_only();
 
-    // stages [0, s_steady) are steady: s + NST - 1 < S and s + 1 < 2*NBF
-    const int s_steady = min(S - (NST - 1), 2 * NBF - 1);
     int s = 0;
-  #pragma unroll 1
-    for (; s + 1 < s_steady; s += 2) {
-      steady_stage(s, std::integral_constant<int, 0>{});
-      steady_stage(s + 1, std::integral_constant<int, 1>{});
+#pragma unroll 1
+    for (; s + 3 < S; s += 4) {
+      stage(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      stage(s + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      stage(s + 2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+      stage(s + 3, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
     }
-    // at most NST stages remain (s is even here)
-    if (s < S) generic_stage(s, std::integral_constant<int, 0>{});
-    if (s + 1 < S) generic_stage(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < S) generic_stage(s + 2, std::integral_constant<int, 0>{});
-    if (s + 3 < S) generic_stage(s + 3, std::integral_constant<int, 1>{});
+    if (s < S) stage(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    if (s + 1 < S) stage(s + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    if (s + 2 < S) stage(s + 2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    // the loads issued past the end are still in flight: drain before the
+    // block's LDS is released
+    wait_vm<0>();
 
     // Any scale outside the exact fp16 range anywhere in the block: leave the
     // block to the exact kernel.
@@ -426,28 +445,31 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S; ++s) {
       __syncthreads();
-      a_issue(s);   // into buffer s % NST
-      b_issue(s, std::integral_constant<int, 0>{});
+      a_issue(s, s);
+      bblk_issue(s >> 1, std::integral_constant<int, 0>{});
       wait_vm<0>();
       __syncthreads();
       const uint8_t* Ab = As + (s % NST) * ASTAGE;
       const int ng = (2 * s + 1 < G) ? 2 : 1;
-      for (int j = 0; j < ng; ++j) {
+      for (int jj = 0; jj < ng; ++jj) {
+        const int g = 2 * (s & 1) + jj;
         h8 B[WN_TILES];
         float sc[WN_TILES];
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t) {
-          const uint32_t w = bw[0][t][j];
-          sc[t] = bf16_to_f32(j ? (bs[0][t] >> 16) : (bs[0][t] & 0xFFFFu));
+          const uint32_t w = bw[0][t][g];
+          const uint32_t pair = bs[0][t][g >> 1];
+          sc[t] = bf16_to_f32((g & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+          uint32_t pr[4];
+          biased_f16_pairs(w, pr);
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            const uint32_t bits = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;
-            const h2 q2 = __builtin_bit_cast(h2, bits) - kOff;
+            const h2 q2 = __builtin_bit_cast(h2, pr[d]) - kOff;
             B[t][2 * d] = q2[0];
             B[t][2 * d + 1] = q2[1];
           }
         }
-        const int apos = j ? apos1 : apos0;
+        const int apos = jj ? apos1 : apos0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
@@ -463,7 +485,8 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
 
   if (!active) return;
   // D element q of row tile i: row 16i + 4*(lane/16) + q, weight row lane%16 of
-  // each tile; the row's activation exponent undoes the fp16 scaling.
+  // each tile; the row's activation exponent undoes the fp16 scaling.  bf16
+  // results are rounded to nearest even by the hardware conversion.
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -474,22 +497,23 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
       const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
       const int ex = a.xexp[src];
       if constexpr (GATED) {
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + row * (N / 2) + r;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const float g = bf16_to_f32(f32_to_bf16(ldexpf(acc[i][t][q], ex)));
-          const float u = bf16_to_f32(f32_to_bf16(ldexpf(acc[i][t + 2][q], ex)));
+          const float g = (float)(__bf16)ldexpf(acc[i][t][q], ex);
+          const float u = (float)(__bf16)ldexpf(acc[i][t + 2][q], ex);
           const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
-          static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)tile[t] * kTileRows + r] =
-              (uint16_t)f32_to_bf16(act * u);
+          orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)(act * u));
         }
-      } else {
+      } else if constexpr (OUT == W4_OUT_F32) {
+        float* orow = static_cast<float*>(a.out) + row * N + r;
 #pragma unroll
-        for (int t = 0; t < WN_TILES; ++t) {
-          const float v = ldexpf(acc[i][t][q], ex);
-          const int64_t o = row * N + (int64_t)tile[t] * kTileRows + r;
-          if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[o] = v;
-          else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16(v);
-        }
+        for (int t = 0; t < WN_TILES; ++t) orow[tile[t] * kTileRows] = ldexpf(acc[i][t][q], ex);
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + row * N + r;
+#pragma unroll
+        for (int t = 0; t < WN_TILES; ++t)
+          orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[i][t][q], ex));
       }
     }
   }

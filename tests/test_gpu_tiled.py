@@ -155,3 +155,25 @@ def test_tiled_linear_exact_integer_case():
         y = w4.linear(bf16_dev(x), to_dev(packed), bf16_dev(layout.encode_scales(sc)), N)
     torch.cuda.synchronize()
     assert np.array_equal(bits_host(y), oracle.linear(x, codes, sc))
+
+
+@pytest.mark.parametrize("kind", ["zero", "tiny", "huge"])
+def test_tiled_gmm_scales_outside_fp16_range(kind):
+    """Blocks whose scales fall outside [2^-14, 2^13) (zero groups, tiny or huge
+    scales) are recomputed by the exact kernel; the others keep the fp16 path.
+    Both must match the oracle."""
+    E, K, N = 4, 704, 256
+    offsets, R, x, row_index, packed, sct, codes, sc = gmm_case(E, 600, K, N, 70 + len(kind))
+    import layout
+    sc = sc.copy()
+    value = {"zero": 0x0000, "tiny": oracle.bf16_from_f64(np.array([3e-6]))[0],
+             "huge": oracle.bf16_from_f64(np.array([2.0e4]))[0]}[kind]
+    sc[1, 5:9, 3] = value          # expert 1: a few groups of a few rows
+    sc[3, 200, :] = value          # expert 3: a whole row
+    sct = np.concatenate([layout.encode_scales(sc[e]) for e in range(E)])
+    say("[tiled gmm out-of-range scales] %s" % kind)
+    got = run_gmm(w4.W4_KERNEL_TILED, offsets, R, x, row_index, packed, sct, E, K, N, w4.W4_EPI_NONE, w4.W4_OUT_F32)
+    ref = ref_gmm(offsets, x, row_index, codes, sc, E, N, w4.W4_EPI_NONE)
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok and not np.isnan(got).any()
