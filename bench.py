@@ -345,13 +345,33 @@ def e2e_report(steps, warmup):
 
 
 # --------------------------------------------------------------------- main
+def copy_report(steps, warmup):
+    """A plain device copy of a known size: the reference for converting the
+    memory-traffic counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
+    dev = torch.device("cuda:0")
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"bytes_read": n, "bytes_written": n, "ms_per_copy": ms, "GBs": 2 * n / (ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="moe-decode",
-                    choices=["moe-decode", "moe-prefill", "dense-decode", "repack", "e2e"])
+                    choices=["moe-decode", "moe-prefill", "dense-decode", "repack", "e2e", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
@@ -400,6 +420,11 @@ def main():
                      "dtype": "fp32 divide / fp64 least squares",
                      "config": {"workload": "repack: 30 layers x 128 experts on-grid bf16 (peak level 4..8)"},
                      "repack": res})
+    elif args.workload == "copy":
+        res = copy_report(args.steps, args.warmup)
+        line.update({"value": res["GBs"], "unit": "GB/s", "ms_per_step": res["ms_per_copy"], "dtype": "u8",
+                     "config": {"workload": "copy: device-to-device copy of 512 MiB (counter calibration)"},
+                     "copy": res})
     else:
         res = e2e_report(args.steps, args.warmup)
         line.update({"value": res["weight_GBs"], "unit": "GB/s", "ms_per_step": res["decode_ms_per_step_30_layers"],

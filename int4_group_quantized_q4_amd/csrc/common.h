@@ -107,6 +107,22 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Gated activations of the MoE epilogues.  gelu with the tanh approximation,
+// tanh(y) = 1 - 2 / (1 + e^(2y)): the absolute error of the hardware exp and
+// reciprocal (~1e-7) moves 0.5 x (1 + tanh) by ~1e-7 relative, far below the
+// bf16 rounding that follows.
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  const float y = c * (x + 0.044715f * x * x * x);
+  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * y));
+  return 0.5f * x * (1.0f + th);
+}
+
+__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// fp32 -> bf16 bits, round to nearest even, by the hardware conversion.
+__device__ __forceinline__ uint16_t bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -52,12 +52,6 @@ constexpr int kWaves = 8;   // waves (weight tiles) per workgroup
 #define W4_DECODE_OCC
 #endif
 
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
-}
-
-__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
 
 // blockIdx -> workgroup index so that consecutive indices (the same expert)
 // land on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
@@ -283,11 +277,10 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
           for (int i = 0; i < 4; ++i) {
             const int64_t row = row0 + 16 * tt + 4 * c + i;
             if (row >= row_end) continue;
-            const float g = bf16_to_f32(f32_to_bf16(acc[tt][i]));
-            const float u = bf16_to_f32(f32_to_bf16(up[i]));
+            const float g = (float)(__bf16)acc[tt][i];
+            const float u = (float)(__bf16)up[i];
             const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
-            static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)unit * kTileRows + r] =
-                (uint16_t)f32_to_bf16(act * u);
+            static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)unit * kTileRows + r] = bf16_rne(act * u);
           }
         }
       }
@@ -302,7 +295,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
             if (row >= row_end) continue;
             const int64_t col = (int64_t)tile * kTileRows + r;
             if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[row * N + col] = acc[tt][i];
-            else static_cast<uint16_t*>(a.out)[row * N + col] = (uint16_t)f32_to_bf16(acc[tt][i]);
+            else static_cast<uint16_t*>(a.out)[row * N + col] = bf16_rne(acc[tt][i]);
           }
         }
       }

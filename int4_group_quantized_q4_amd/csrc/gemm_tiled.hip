@@ -75,17 +75,6 @@ constexpr unsigned kScaleLo = 0x3880u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr unsigned kScaleSpan = 0x0D80u;
 
-// gelu with the tanh approximation, tanh(y) = 1 - 2 / (1 + e^(2y)): the
-// absolute error of the hardware exp and reciprocal (~1e-7) moves
-// 0.5 x (1 + tanh) by ~1e-7 relative, far below the bf16 rounding that follows.
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  const float y = c * (x + 0.044715f * x * x * x);
-  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * y));
-  return 0.5f * x * (1.0f + th);
-}
-
-__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ f32x4 mfma_f16(h8 a, h8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
