@@ -184,6 +184,8 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
  *                     fp16's finest step).  A block meeting a scale outside that
  *                     range is recomputed by a second kernel with per-group
  *                     fp32 scaling.
+ * One (expert's) weight matrix must stay below 2 GiB of codes (N*K/2 < 2^31),
+ * else W4_ERR_SHAPE.
  * The tiled kernel needs a workspace for the fp16 activation rows:
  * w4a16_linear_workspace / w4a16_moe_gmm_workspace bytes, 16-byte aligned.  A
  * call that selects the tiled kernel (w4a16_set_gemm_kernel) without enough

@@ -97,6 +97,8 @@ int w4a16_set_gemm_kernel(int kernel) {
 static int run_gemm(const w4::GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   // Average rows per expert decides the kernel: weight-streaming (decode) or
   // LDS-tiled MFMA (prefill, needs the workspace for the fp16 activations).
+  // the kernels address one expert's codes through 32-bit buffer offsets
+  if (a.N * a.K / 2 >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
   const int policy = g_gemm_kernel.load(std::memory_order_relaxed);
   bool tiled = w4::gemm_tiled_supported(a);
   if (policy == W4_KERNEL_STREAM) tiled = false;

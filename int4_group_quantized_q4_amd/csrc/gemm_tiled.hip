@@ -303,8 +303,11 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     const uint32_t sva = sv & ~3u, ssh = (sv & 3u) * 8u;
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) {
-      bw[sl][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv, wtoff[t] + 1024 * blk, 0));
-      const uint64_t sc64 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, sva, stoff[t] + 128 * blk, 0));
+      // whole offsets in the VGPR operand: the buffer's range check covers
+      // them, so the partial block's over-reads at the matrix end return zeros
+      bw[sl][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv + wtoff[t] + 1024 * blk, 0, 0));
+      const uint64_t sc64 =
+          __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, sva + stoff[t] + 128 * blk, 0, 0));
       bs[sl][t] = __builtin_bit_cast(u32x2, sc64 >> ssh);
     }
   };
