@@ -40,17 +40,12 @@ constexpr int kWaves = 8;   // waves (weight tiles) per workgroup
 #ifndef W4_DECODE_RING
 #define W4_DECODE_RING 4
 #endif
+// Occupancy the register allocation aims for (waves per SIMD): 4 for one
+// 16-row tile of activation rows (two 8-wave workgroups per CU), 2 for two.
 #ifndef W4_DECODE_WAVES_PER_SIMD
 #define W4_DECODE_WAVES_PER_SIMD 4
 #endif
-#ifndef W4_DECODE_SERIAL
-#define W4_DECODE_SERIAL 0
-#endif
-#if W4_DECODE_WAVES_PER_SIMD > 0
-#define W4_DECODE_OCC __attribute__((amdgpu_waves_per_eu(W4_DECODE_WAVES_PER_SIMD)))
-#else
-#define W4_DECODE_OCC
-#endif
+#define W4_DECODE_OCC __attribute__((amdgpu_waves_per_eu(MAXT == 1 ? W4_DECODE_WAVES_PER_SIMD : 2)))
 
 
 // blockIdx -> workgroup index so that consecutive indices (the same expert)
@@ -75,6 +70,11 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   constexpr int XBUF = 16 * MAXT * XS;                       // one staging buffer
   constexpr int EXBYTES = (kWaves / 2) * MAXT * 64 * 16;     // gate/up hand-over
   __shared__ __align__(16) uint8_t xs[2 * XBUF > EXBYTES ? 2 * XBUF : EXBYTES];
+  // scale spans: SPB blocks (a whole number of chunks, at least 8), 128 B each
+  constexpr int SPB = CB > 8 ? CB : 8;
+  constexpr int SPBYTES = SPB * 128;
+  constexpr int SPL = SPB / 8;   // 16-byte loads per lane per span
+  __shared__ __align__(16) uint8_t ssc[kWaves * SPBYTES];
 
   const int wg = xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
@@ -114,10 +114,33 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   const uint16_t* sb = a.scales + ((int64_t)e * N + (int64_t)tile * kTileRows) * G;
 
   u32x4 cw[D];
-  u32x2 sw[D];
   auto load_block = [&](int slot, int b) __attribute__((always_inline)) {
     cw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + 1024 * (int64_t)b + 16 * lane));
-    sw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sb + 64 * (int64_t)b + 4 * r));
+  };
+
+  // Scales of the full blocks travel in spans of SPB blocks (contiguous in the
+  // tile's scale layout): 128-bit loads, one per lane per 8 blocks, parked in
+  // this wave's LDS span buffer, then 8 bytes per lane per block from there.
+  // The next span overwrites the buffer after the wave's last read of the
+  // current one (LDS accesses of one wave complete in order).  Per-block
+  // 128-byte scale loads would make a second, sparse stream beside the codes.
+  // The loads go through a buffer descriptor over the expert's scales: lanes
+  // past the tile's last full block read the tail block or the next tile, and
+  // past the end of the expert get zeros; those bytes are never used.
+  uint8_t* mys = ssc + wv * SPBYTES;
+  const int NSP = (NBF + SPB - 1) / SPB;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), 0x00020000);
+  const uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
+  auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      t[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           srs, sv_lane, (uint32_t)(SPBYTES * sp + 1024 * i), 0));
+  };
+  auto span_store = [&](const u32x4* t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) *reinterpret_cast<u32x4*>(mys + 1024 * i + 16 * lane) = t[i];
   };
 
   // the partial last block (1..3 groups), loaded once
@@ -183,6 +206,9 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     __syncthreads();   // the previous pass is done with both buffers
     stage_load(0);
     if (NBF > 0) {
+      u32x4 s0[SPL];
+      span_load(s0, 0);
+      span_store(s0);
 #pragma unroll
       for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
     }
@@ -199,8 +225,8 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
 
     // one block: MFMAs on the slot's codes, then refill the slot with block bn
     // (after the slot's last use, so no register copies are needed)
-    auto do_block = [&](const uint8_t* xb, int lb, int slot, int bn) __attribute__((always_inline)) {
-      const u32x2 sv = sw[slot];
+    auto do_block = [&](const uint8_t* xb, int b, int lb, int slot, int bn) __attribute__((always_inline)) {
+      const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + (b % SPB) * 128 + 8 * r);
       const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16),
                            bf16_to_f32(sv[1] & 0xFFFFu), bf16_to_f32(sv[1] >> 16)};
 #pragma unroll
@@ -220,26 +246,43 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     };
 
     // full chunks: straight-line code, every load unconditional (indices clamped)
+    // (a span is a whole number of chunks: its next span is loaded at its
+    // first chunk and parked after its last)
+    static_assert(SPB % CB == 0, "a scale span must cover whole chunks");
+    constexpr int CPS = SPB / CB;   // chunks per span
     const int nfull = NBF / CB;
-    for (int ch = 0; ch < nfull; ++ch) {
+    auto do_chunk = [&](int ch) __attribute__((always_inline)) {
       const int chn = ch + 1 < nch ? ch + 1 : nch - 1;
       stage_load(chn);
       const uint8_t* xb = xs + (ch & 1) * XBUF;
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb) {
         const int bn = ch * CB + lb + D;
-        do_block(xb, lb, lb % D, bn < NBF ? bn : NBF - 1);
+        do_block(xb, ch * CB + lb, lb, lb % D, bn < NBF ? bn : NBF - 1);
       }
       stage_store(chn);
       __syncthreads();
+    };
+    // whole spans of full chunks: the next span's scales are loaded at the
+    // span's first chunk and parked after its last, unconditionally (past
+    // the last span they are junk that no block reads)
+    const int nspan_full = nfull / CPS;
+    for (int sp = 0; sp < nspan_full; ++sp) {
+      u32x4 snext[SPL];
+      span_load(snext, sp + 1);
+#pragma unroll
+      for (int k = 0; k < CPS; ++k) do_chunk(sp * CPS + k);
+      span_store(snext);
     }
+    // the remaining full chunks, in the span parked last
+    for (int ch = nspan_full * CPS; ch < nfull; ++ch) do_chunk(ch);
     // the last, partial chunk: remaining full blocks and the partial block
     if (nfull < nch) {
       const int ch = nfull;
       const uint8_t* xb = xs + (ch & 1) * XBUF;
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb)
-        if (ch * CB + lb < NBF) do_block(xb, lb, lb % D, NBF - 1);
+        if (ch * CB + lb < NBF) do_block(xb, ch * CB + lb, lb, lb % D, NBF - 1);
       if (gtail > 0) {
         const int lb = NBF - ch * CB;   // local index of the partial block
 #pragma unroll

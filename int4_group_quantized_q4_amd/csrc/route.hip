@@ -6,15 +6,16 @@
 // token) and section "What changed in vLLM's TPU backend" (the experts' rows
 // are handed to a grouped-matmul backend).
 //
-// Top-k: one wave per token.  The token's logits go to LDS; every lane ranks
-// its own logits against all E (rank = number of logits that are larger, or
-// equal with a lower id), so the logits with rank < k are the top k and the
-// rank is their slot -- no dependent cross-lane reduction chain.  Softmax
-// max/sum use wave butterflies.
+// Top-k: one wave per token, lane l holding logits l, l+64, ...  Slot j is a
+// wave-wide argmax over the logits not yet taken: DPP max within each 16-lane
+// row, four readlanes across the rows, then ballots pick the lowest id holding
+// that maximum (ties go to the lower id).  The first round's maximum is the
+// softmax shift; the sum is one butterfly.
 //
 // Sort: the T*k routed rows r = t*k + j are grouped by expert, keeping r order
-// within an expert.  Small plans (R <= kSmallRows) use one workgroup that
-// counts, ranks, scans and scatters.  Larger plans use chunks of the rows:
+// within an expert.  Small plans (R <= kSmallRows) are sorted by one
+// workgroup that counts, ranks, scans and scatters.  Larger plans use chunks
+// of the rows:
 // a kernel ranks each chunk's rows within their expert (ballot-based match
 // inside each wave, prefix over the waves), one block scans the chunk counts
 // into offsets, and a scatter kernel writes the permutation.
@@ -26,7 +27,7 @@ namespace w4 {
 
 namespace {
 
-constexpr int kTopkWaves = 8;       // tokens per top-k workgroup
+constexpr int kTopkWaves = 2;       // tokens per top-k workgroup (spread over many CUs)
 constexpr int kChunkThreads = 256;  // routed rows per ranking chunk
 constexpr int kSmallRows = 4096;    // single-workgroup sort up to this many rows
 constexpr int kSmallThreads = 1024;
@@ -37,65 +38,75 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per token: ids[t][0..k) by descending logit (ties: lower id first)
-// and their softmax probabilities.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror: every lane holds its row's max
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Token t on one wave: ids[t][0..k) by descending logit (ties: lower id
+// first) and their softmax probabilities.  E <= 64*S <= 256, k <= E, finite
+// logits.
+template <int S>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int64_t t, int E, int k, int lane,
+                                           int32_t* __restrict__ ids, float* __restrict__ weights) {
+  float v[S];
+  bool live[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = lane + 64 * s;
+    live[s] = e < E;
+    v[s] = live[s] ? logits[t * E + e] : -INFINITY;
+  }
+  unsigned taken = 0;
+  float mx = 0.f, sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float cand = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (live[s] && !((taken >> s) & 1u)) cand = fmaxf(cand, v[s]);
+    const float m = wave_max_all(cand);
+    if (j == 0) {
+      mx = m;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (live[s]) sum += expf(v[s] - mx);
+      sum = wave_sum(sum);
+    }
+    int sel = -1;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint64_t bal = __ballot(live[s] && !((taken >> s) & 1u) && v[s] == m);
+      if (sel < 0 && bal != 0ull) sel = 64 * s + __builtin_ctzll(bal);
+    }
+    if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
+    if (lane == 0) {
+      ids[t * k + j] = sel;
+      weights[t * k + j] = expf(m - mx) / sum;
+    }
+  }
+}
+
+template <int S>
 __global__ void __launch_bounds__(64 * kTopkWaves) topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                                int k, int32_t* __restrict__ ids,
                                                                float* __restrict__ weights) {
-  __shared__ float s_v[kTopkWaves][256];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kTopkWaves + wv;
+  const int64_t t = (int64_t)blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= T) return;   // wave-uniform; no barriers in this kernel
-  float v[4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int e = lane + 64 * s;
-    v[s] = e < E ? logits[t * E + e] : -INFINITY;
-    if (e < E) s_v[wv][e] = v[s];
-    mx = fmaxf(mx, v[s]);
-  }
-  mx = wave_max(mx);
-  float sum = 0.0f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    if (lane + 64 * s < E) sum += expf(v[s] - mx);
-  sum = wave_sum(sum);
-  // the wave's LDS writes are visible to the wave after this fence
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  int rank[4] = {0, 0, 0, 0};
-  const int E4 = E & ~3;
-  for (int e0 = 0; e0 < E4; e0 += 4) {
-    const float4 w = *reinterpret_cast<const float4*>(&s_v[wv][e0]);
-    const float wvv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + q;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int me = lane + 64 * s;
-        rank[s] += (wvv[q] > v[s] || (wvv[q] == v[s] && e < me)) ? 1 : 0;
-      }
-    }
-  }
-  for (int e = E4; e < E; ++e) {
-    const float w = s_v[wv][e];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int me = lane + 64 * s;
-      rank[s] += (w > v[s] || (w == v[s] && e < me)) ? 1 : 0;
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int e = lane + 64 * s;
-    if (e < E && rank[s] < k) {
-      ids[t * k + rank[s]] = e;
-      weights[t * k + rank[s]] = expf(v[s] - mx) / sum;
-    }
-  }
+  topk_token<S>(logits, t, E, k, lane, ids, weights);
 }
 
 // rank of each lane's row among the wave's rows with the same expert id
@@ -119,18 +130,21 @@ __global__ void __launch_bounds__(kSmallThreads) sort_small_kernel(const int32_t
                                                                   int32_t* __restrict__ sorted_tokens,
                                                                   int32_t* __restrict__ row_to_sorted) {
   constexpr int NW = kSmallThreads / 64;
+  __shared__ int s_ids[kSmallRows];
   __shared__ int s_cnt[NW][256];   // per-wave counts of the current pass
   __shared__ int s_base[256];      // rows of each expert seen in earlier passes
   __shared__ int s_off[257];
+  __shared__ int s_wtot[4];
   __shared__ int s_rank[kSmallRows];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int r = tid; r < R; r += kSmallThreads) s_ids[r] = ids[r];
   for (int x = tid; x < 256; x += kSmallThreads) s_base[x] = 0;
   for (int r0 = 0; r0 < R; r0 += kSmallThreads) {
     for (int x = tid; x < NW * 256; x += kSmallThreads) (&s_cnt[0][0])[x] = 0;
     __syncthreads();
     const int r = r0 + tid;
     const bool live = r < R;
-    const int e = live ? ids[r] : 0x1ff;
+    const int e = live ? s_ids[r] : 0x1ff;
     int rw, grp;
     wave_match(e, lane, rw, grp);
     if (live && rw == 0) s_cnt[wv][e] = grp;
@@ -148,19 +162,29 @@ __global__ void __launch_bounds__(kSmallThreads) sort_small_kernel(const int32_t
     }
     __syncthreads();   // the next pass clears s_cnt
   }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int x = 0; x < E; ++x) {
-      s_off[x] = run;
-      run += s_base[x];
+  // exclusive scan of the E <= 256 counts: waves 0..3 scan 64 each
+  int incl = 0, own = 0;
+  if (tid < 256) {
+    own = tid < E ? s_base[tid] : 0;
+    incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int up = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += up;
     }
-    s_off[E] = run;
+    if (lane == 63) s_wtot[wv] = incl;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += s_wtot[w];
+    if (tid < E) s_off[tid] = before + incl - own;
+    if (tid == E - 1) s_off[E] = before + incl;
   }
   __syncthreads();
   for (int x = tid; x <= E; x += kSmallThreads) offsets[x] = s_off[x];
   for (int r = tid; r < R; r += kSmallThreads) {
-    const int pos = s_off[ids[r]] + s_rank[r];
+    const int pos = s_off[s_ids[r]] + s_rank[r];
     sorted_rows[pos] = r;
     sorted_tokens[pos] = r / k;
     row_to_sorted[r] = pos;
@@ -269,8 +293,10 @@ void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t*
     return;
   }
   const int64_t R = T * k;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), dim3(64 * kTopkWaves), 0,
-                     stream, logits, T, E, k, ids, weights);
+  const dim3 tg((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), tb(64 * kTopkWaves);
+  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+  else hipLaunchKernelGGL(topk_kernel<4>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
   if (R <= kSmallRows) {
     hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, ids, (int)R, E, k, offsets,
                        sorted_rows, sorted_tokens, row_to_sorted);

@@ -39,7 +39,8 @@ def test_route_moe_prefill_zipf():
     check_route(logits, cfg["k"], "moe-prefill")
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (37, 16, 3), (33, 256, 16), (5, 8, 8), (300, 64, 1), (1000, 128, 8)])
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (37, 16, 3), (33, 256, 16), (5, 8, 8), (300, 64, 1), (1000, 128, 8),
+                                   (512, 128, 8), (513, 128, 8)])   # R = 4096: largest one-workgroup plan
 def test_route_shapes_and_ties(T, E, k):
     rng = gen.rng_for(930, T + E + k)
     logits = gen.router_logits(rng, T, E)
