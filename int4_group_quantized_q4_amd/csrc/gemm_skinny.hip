@@ -203,14 +203,16 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       for (int q = 0; q < NP; ++q) *reinterpret_cast<u32x4*>(buf + xdst[q]) = xr[q];
     };
 
+    // every load of the pass's start is issued before the first wait: the
+    // first chunk's activations, the first scale span, the ring's blocks
     __syncthreads();   // the previous pass is done with both buffers
     stage_load(0);
     if (NBF > 0) {
       u32x4 s0[SPL];
       span_load(s0, 0);
-      span_store(s0);
 #pragma unroll
       for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+      span_store(s0);
     }
     stage_store(0);
     __syncthreads();
