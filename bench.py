@@ -254,13 +254,14 @@ def dense_decode_report(steps, warmup):
     for M in cfg["Ms"]:
         x = gen.bf16_normal_t(g, (M, K), dev)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
         for i in range(warmup):
-            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y)
+            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):
-            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y)
+            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps

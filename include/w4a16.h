@@ -186,10 +186,16 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
  *                     fp32 scaling.
  * One (expert's) weight matrix must stay below 2 GiB of codes (N*K/2 < 2^31),
  * else W4_ERR_SHAPE.
- * The tiled kernel needs a workspace for the fp16 activation rows:
- * w4a16_linear_workspace / w4a16_moe_gmm_workspace bytes, 16-byte aligned.  A
- * call that selects the tiled kernel (w4a16_set_gemm_kernel) without enough
- * workspace returns W4_ERR_WORKSPACE; the streaming kernel ignores ws.
+ *   split-K kernel    (w4a16_linear with M <= 16 and fewer than 4096 16-row
+ *                     tiles) the streaming kernel's products, per 1024-column
+ *                     slice of K; the slices' fp32 partial sums go to the
+ *                     workspace and are added in slice order.
+ * The tiled kernel needs a workspace for the fp16 activation rows, the split-K
+ * kernel one for its partial sums: w4a16_linear_workspace /
+ * w4a16_moe_gmm_workspace bytes, 16-byte aligned.  A call that selects the
+ * tiled kernel (w4a16_set_gemm_kernel) without enough workspace returns
+ * W4_ERR_WORKSPACE; without enough workspace for the split-K kernel the
+ * streaming kernel runs instead (which ignores ws).
  */
 
 /*

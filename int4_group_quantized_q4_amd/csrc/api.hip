@@ -108,6 +108,9 @@ static int run_gemm(const w4::GemmArgs& a, void* ws, size_t ws_bytes, hipStream_
       return W4_ERR_WORKSPACE;
     }
     w4::launch_gemm_tiled(a, ws, stream);
+  } else if (w4::gemm_splitk_supported(a) && ws && aligned16(ws) &&
+             ws_bytes >= w4::gemm_splitk_workspace(a.R, a.K, a.N)) {
+    w4::launch_gemm_splitk(a, ws, stream);   // few tiles: split K over more waves
   } else {
     w4::launch_gemm_skinny(a, stream);
   }
@@ -116,7 +119,9 @@ static int run_gemm(const w4::GemmArgs& a, void* ws, size_t ws_bytes, hipStream_
 
 size_t w4a16_linear_workspace(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K < 0 || N < 0) return 0;
-  return w4::gemm_tiled_workspace(M, M, 1, K, N);
+  const size_t tiled = w4::gemm_tiled_workspace(M, M, 1, K, N);
+  const size_t splitk = w4::gemm_splitk_workspace(M, K, N);
+  return tiled > splitk ? tiled : splitk;
 }
 
 size_t w4a16_moe_gmm_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N) {

@@ -1,0 +1,198 @@
+// Dense decode-shaped W4A16 matmul split along K: one weight matrix, at most
+// 16 activation rows.
+//
+// [RQ] "Repacked QAT Gemma 4 26B-A4B serves on one TPU v6e at 1.9x FP8
+// throughput", section "What changed in vLLM's TPU backend": one scale per
+// 32-wide group, each weight tile dequantized on chip before the multiply,
+// activations in bf16.  "What quantization really is", section "Why the tip
+// exists": generation rereads the weights token by token, so the kernel is
+// bound by the weight bytes it streams.
+//
+// One wave per 16-row weight tile streams its whole K in the weight-streaming
+// kernel; a matrix of few tiles (14336 rows = 896 tiles) then keeps only a
+// third of the chip's SIMDs busy.  Here the K axis is cut into slices of 8
+// tile16 blocks (1024 columns): a workgroup of 8 waves takes one slice of 8
+// tiles, so the launch has tiles x slices waves.  Each wave issues its 8 code
+// blocks (one 128-bit load per lane each) and its 1 KiB scale span before any
+// wait, so a workgroup waits for memory once.  The slice of the activation
+// rows is staged in LDS once per workgroup.  Per group the partial dot
+// products come out of the matrix core as in the streaming kernel (bf16 128+u
+// codes, a -136 operand for the bias, fp32 scale per group on the VALU).
+// Slices write fp32 partial sums to the workspace; a second kernel adds the
+// slices and rounds.
+
+#include "common.h"
+#include "internal.h"
+#include "w4a16.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int kSKWaves = 8;                         // weight tiles per workgroup
+constexpr int kSliceBlocks = 8;                     // tile16 blocks per K-slice
+constexpr int kSliceCols = kSliceBlocks * 128;      // 1024
+constexpr int kXStride = kSliceCols * 2 + 16;       // LDS row stride: 16 B off the 256 B bank period
+constexpr int kMaxRows = 16;
+constexpr int kRsrcFlags = 0x00020000;              // raw buffer descriptor word 3
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+int slices_of(int64_t K) {
+  const int64_t G = K / kGroup;
+  const int64_t nb = (G + kBlockGroups - 1) / kBlockGroups;   // blocks, the partial one included
+  return (int)((nb + kSliceBlocks - 1) / kSliceBlocks);
+}
+
+// grid: (tile groups) x (slices), slice fastest.  part: [slices][R][N] fp32.
+__global__ void __launch_bounds__(64 * kSKWaves) splitk_partial_kernel(GemmArgs a, int nslices, float* part) {
+  __shared__ __align__(16) uint8_t xs[kMaxRows * kXStride];
+  __shared__ __align__(16) uint8_t ssc[kSKWaves * 1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int s = blockIdx.x % nslices;
+  const int tg = blockIdx.x / nslices;
+  const int M = (int)a.R;
+  const int64_t K = a.K, N = a.N;
+  const int G = (int)(K / kGroup);
+  const int NBF = G / kBlockGroups;
+  const int gtail = G - NBF * kBlockGroups;
+  const int tiles = (int)(N / kTileRows);
+  int tile = tg * kSKWaves + wv;
+  const bool active = tile < tiles;
+  if (!active) tile = tiles - 1;   // idle waves re-read a valid tile and store nothing
+
+  const int kb0 = s * kSliceBlocks;
+  const int nb = NBF - kb0 < kSliceBlocks ? NBF - kb0 : kSliceBlocks;   // full blocks of the slice (may be 0)
+  const bool tail = gtail > 0 && s == nslices - 1;
+  const int64_t col0 = (int64_t)s * kSliceCols;
+  const int ncols = (int)(K - col0 < kSliceCols ? K - col0 : kSliceCols);
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.qweight, 0, (int)(N * K / 2), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)a.scales, 0, (int)(N * G * 2), kRsrcFlags);
+  const uint32_t wtile = (uint32_t)tile * (uint32_t)(8 * K);
+  const uint32_t stile = (uint32_t)tile * (uint32_t)(32 * G);
+
+  // 1. every weight load of the wave: 8 code blocks (past the slice's last
+  // full block they re-read it), the slice's 1 KiB scale span (lane l: block
+  // l/8, rows 2(l%8) and 2(l%8)+1; past the matrix the descriptor returns
+  // zeros), and the partial block's codes and scales
+  u32x4 cw[kSliceBlocks];
+  u32x4 sv = {0u, 0u, 0u, 0u};
+  if (nb > 0) {
+#pragma unroll
+    for (int i = 0; i < kSliceBlocks; ++i) {
+      const int bb = kb0 + (i < nb ? i : nb - 1);
+      cw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wtile + 1024u * bb + 16u * lane, 0, 0));
+    }
+    sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, stile + 128u * kb0 + 16u * lane, 0, 0));
+  }
+  uint32_t ct[3] = {0u, 0u, 0u};
+  float st[3] = {0.f, 0.f, 0.f};
+  if (tail) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < gtail) {
+        ct[j] = __builtin_amdgcn_raw_buffer_load_b32(rw, wtile + 1024u * NBF + 4u * gtail * lane + 4u * j, 0, 0);
+        st[j] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, stile + 128u * NBF + 2u * (r * gtail + j), 0, 0));
+      }
+  }
+
+  // 2. the slice of the activation rows (rows < M only) into LDS
+  const int ppr = ncols / 8;   // 16-byte pieces per row
+  for (int p = (int)threadIdx.x; p < M * ppr; p += 64 * kSKWaves) {
+    const int m = p / ppr, pc = p - m * ppr;
+    const int64_t row = a.row_index ? (int64_t)a.row_index[m] : (int64_t)m;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + row * K + col0 + 8 * pc);
+    *reinterpret_cast<u32x4*>(xs + m * kXStride + 16 * pc) = v;
+  }
+  uint8_t* mys = ssc + wv * 1024;
+  *reinterpret_cast<u32x4*>(mys + 16 * lane) = sv;
+  __syncthreads();
+
+  // 3. the slice's blocks: D rows = 4c + i, column = r
+  const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int arow = r < M ? r : 0;   // rows past M read row 0; their results are never stored
+  const uint8_t* xa = xs + arow * kXStride + c * 16;
+  f32x4 acc = zero4;
+#pragma unroll
+  for (int i = 0; i < kSliceBlocks; ++i) {
+    if (i >= nb) break;
+    const u32x2 sp = *reinterpret_cast<const u32x2*>(mys + 128 * i + 8 * r);
+    const float sc[4] = {bf16_to_f32(sp[0] & 0xFFFFu), bf16_to_f32(sp[0] >> 16), bf16_to_f32(sp[1] & 0xFFFFu),
+                         bf16_to_f32(sp[1] >> 16)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (i * 4 + j) * 64);
+      const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+      const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(cw[i][j])), cb);
+      acc += sc[j] * p;
+    }
+  }
+  if (tail) {
+    const int lb = nb > 0 ? nb : 0;   // the partial block follows the slice's full blocks
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < gtail) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (lb * 4 + j) * 64);
+        const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+        const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(ct[j])), cb);
+        acc += st[j] * p;
+      }
+  }
+
+  if (active) {
+    float* dst = part + ((int64_t)s * M) * N + (int64_t)tile * kTileRows + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * c + i < M) dst[(int64_t)(4 * c + i) * N] = acc[i];
+  }
+}
+
+// y[m][n] = sum over slices of part[s][m][n], stored as fp32 or bf16.
+template <int OUT>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nslices, int64_t MN,
+                                                            void* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < nslices; ++s) v += *reinterpret_cast<const f32x4*>(part + (int64_t)s * MN + i);
+  if constexpr (OUT == W4_OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = v;
+  } else {
+    u32x2 o;
+    o[0] = (uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16);
+    o[1] = (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i) = o;
+  }
+}
+
+}  // namespace
+
+bool gemm_splitk_supported(const GemmArgs& a) {
+  return a.E == 1 && !a.offsets && a.epilogue == W4_EPI_NONE && a.R >= 1 && a.R <= kMaxRows &&
+         slices_of(a.K) >= 2 && (a.N / kTileRows) < 4096;
+}
+
+size_t gemm_splitk_workspace(int64_t R, int64_t K, int64_t N) {
+  if (R < 1 || R > kMaxRows || K < kGroup) return 0;
+  return (size_t)slices_of(K) * (size_t)R * (size_t)N * sizeof(float);
+}
+
+void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream) {
+  const int ns = slices_of(a.K);
+  const int tgs = (int)((a.N / kTileRows + kSKWaves - 1) / kSKWaves);
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(splitk_partial_kernel, dim3((unsigned)(tgs * ns)), dim3(64 * kSKWaves), 0, stream, a, ns, part);
+  const int64_t MN = a.R * a.N;
+  const dim3 rg((unsigned)((MN / 4 + 255) / 256));
+  if (a.out_dtype == W4_OUT_F32)
+    hipLaunchKernelGGL(splitk_reduce_kernel<W4_OUT_F32>, rg, dim3(256), 0, stream, part, ns, MN, a.out);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<W4_OUT_BF16>, rg, dim3(256), 0, stream, part, ns, MN, a.out);
+}
+
+}  // namespace w4

@@ -68,3 +68,34 @@ def test_linear_empty_M():
     y = torch.full((0, 32), 7.0, dtype=torch.bfloat16, device="cuda")
     w4.w4a16_linear(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), to_dev(packed), bf16_dev(sc), 32, y)
     torch.cuda.synchronize()
+
+
+# Split-K kernel (M <= 16, K over 1024 columns, with a workspace): a last
+# slice holding only the partial block (K = 1088, 1056), 1..3 tail groups,
+# tile groups with idle waves (N/16 not a multiple of 8), several slices.
+@pytest.mark.parametrize("M,K,N", [(1, 1088, 48), (16, 1056, 32), (7, 4096, 144), (16, 2816, 16),
+                                   (9, 9216, 64), (3, 1120, 128)])
+def test_linear_splitk_shapes(M, K, N):
+    check_linear(M, K, N, 300 + M + K + N, "split-K %dx%dx%d" % (M, K, N))
+
+
+def test_linear_splitk_agrees_with_streaming():
+    """The same call without a workspace runs the streaming kernel: both match
+    the oracle and each other (they differ in fp32 summation order only)."""
+    rng = gen.rng_for(920, 9)
+    M, K, N = 16, 4096, 256
+    packed, sct, codes, sc = linear_weights(rng, N, K)
+    x = gen.bf16_normal(rng, (M, K))
+    xd, qd, sd = bf16_dev(x), to_dev(packed), bf16_dev(sct)
+    y_split = w4.linear(xd, qd, sd, N)
+    y_stream = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_linear(xd, qd, sd, N, y_stream)
+    torch.cuda.synchronize()
+    ref = oracle.bf16_bits_to_f64(oracle.linear(x, codes, sc))
+    for y in (y_split, y_stream):
+        ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y)), ref)
+        say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+        assert ok
+    ok, _, _ = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y_split)),
+                                       oracle.bf16_bits_to_f64(bits_host(y_stream)))
+    assert ok
