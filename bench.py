@@ -44,6 +44,34 @@ BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
 EXPERT_W1_BYTES = 1408 * 2816 // 2 + 1408 * 88 * 2   # 2,230,272
 EXPERT_W2_BYTES = 2816 * 704 // 2 + 2816 * 22 * 2    # 1,115,136
 
+# HBM bytes per launch of the two roofline kernels, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes over this bench (profiles/gemm_hbm_traffic.md): reads scaled
+# by 2.000 and writes by 1.000, the factors a 512 MiB device copy gives.  They
+# hold only for the sources they were taken on (sha256 of the listed files in
+# csrc/, in order); once one changes, the bench reports traffic as null.
+TRAFFIC = {
+    "decode_gmm1": {"sources": ("gemm_skinny.hip", "common.h", "internal.h"),
+                    "sha256": "32caec3fbbe962886f5427878bd2441a465a05d3adea52eec85bacd9fad8c462",
+                    "read_bytes": 289680435, "write_bytes": 720896},
+    "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
+                     "sha256": "2607194e83746317de6ce10b6c690fd659feaca003918d46a2b8424c91ca9779",
+                     "read_bytes": 540630868, "write_bytes": 46152704},
+}
+
+
+def traffic_of(key):
+    """Counter-measured HBM bytes (read + write) per launch, or None when the
+    kernel's sources differ from those the counters were taken on."""
+    import hashlib
+    rec = TRAFFIC[key]
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "int4_group_quantized_q4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sha256"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
@@ -163,7 +191,7 @@ def moe_decode_report(steps, warmup):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": w1bytes / (r["gmm1_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic_of("decode_gmm1"),
         },
     }
     return out, r["layerset"]
@@ -193,7 +221,7 @@ def moe_prefill_report(steps, warmup):
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops1 / (r["gmm1_ms"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic_of("prefill_gmm1"),
         },
     }
 
