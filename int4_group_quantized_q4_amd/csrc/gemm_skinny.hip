@@ -34,6 +34,7 @@ namespace w4 {
 namespace {
 
 constexpr int kWaves = 8;   // waves (weight tiles) per workgroup
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
 // Ring depth of the many-tile (MoE) path and the occupancy its register
 // allocation aims for (waves per SIMD; 0 = compiler default).
@@ -130,7 +131,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   uint8_t* mys = ssc + wv * SPBYTES;
   const int NSP = (NBF + SPB - 1) / SPB;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), 0x00020000);
+      (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
   const uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
   auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) {
 #pragma unroll
@@ -171,30 +172,41 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     const int ntt = (cnt + 15) >> 4;
     const int nch = (NBall + CB - 1) / CB;
 
-    // this thread's staging pieces: source pointers fixed for the pass.  Rows
-    // beyond the count re-read row 0 and columns past K are clamped, so the
-    // loads need no branches; those LDS bytes are never read as operands.
-    const uint16_t* xsrc[NP];
+    // this thread's staging pieces: one buffer descriptor per piece row,
+    // fixed for the pass.  A row is staged by whole waves (a row's pieces are
+    // 64 consecutive threads), so each descriptor is wave-uniform.  Rows
+    // beyond the count get an empty range: their loads return zeros without
+    // touching memory (those LDS rows are never read as operands: their lanes
+    // read row 0).  Columns past K are clamped.
+    static_assert(PPR % 64 == 0, "a staged row must cover whole waves");
+    __amdgpu_buffer_rsrc_t xrs[NP];
     int xdst[NP];
-    int xcol[NP];
+    uint32_t xoff[NP];
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const int p = (int)threadIdx.x + q * 64 * kWaves;
-      const int rr = p / PPR;
+      const int rr = __builtin_amdgcn_readfirstlane(p / PPR);
       const int pc = p - rr * PPR;
-      const int64_t srow = rr < cnt ? (a.row_index ? (int64_t)a.row_index[row0 + rr] : row0 + rr)
-                                    : (a.row_index ? (int64_t)a.row_index[row0] : row0);
-      xsrc[q] = a.x + srow * K;
+      const bool live = rr < cnt;
+      const int64_t srow = live ? (a.row_index ? (int64_t)a.row_index[row0 + rr] : row0 + rr)
+                                : (a.row_index ? (int64_t)a.row_index[row0] : row0);   // a valid row
+      // (readfirstlane returns int: each half goes back through uint32_t so
+      // the low half is not sign-extended into the high one)
+      const uint64_t base = (uint64_t)(a.x + srow * K);
+      const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+      const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+      const uint64_t ub = ((uint64_t)bhi << 32) | (uint64_t)blo;
+      xrs[q] = __builtin_amdgcn_make_buffer_rsrc((void*)ub, 0, live ? (int)(K * 2) : 0, kRsrcFlags);
       xdst[q] = rr * XS + pc * 16;
-      xcol[q] = pc * 8;
+      xoff[q] = (uint32_t)(pc * 16);
     }
     u32x4 xr[NP];
     auto stage_load = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
-        int64_t col = (int64_t)ch * KC + xcol[q];
-        col = col < K - 8 ? col : K - 8;
-        xr[q] = *reinterpret_cast<const u32x4*>(xsrc[q] + col);
+        uint32_t off = (uint32_t)(ch * KC * 2) + xoff[q];
+        off = off < (uint32_t)(K * 2 - 16) ? off : (uint32_t)(K * 2 - 16);
+        xr[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[q], off, 0, 0));
       }
     };
     auto stage_store = [&](int ch) __attribute__((always_inline)) {
