@@ -41,6 +41,11 @@ constexpr int kRsrcFlags = 0x00020000;   // raw buffer descriptor word 3 (32-bit
 #ifndef W4_DECODE_RING
 #define W4_DECODE_RING 4
 #endif
+// Short K (at most 8 tile16 blocks) with a plain epilogue goes to the
+// several-tiles-per-wave kernel (gemm_short.hip).
+#ifndef W4_DECODE_SHORT_K
+#define W4_DECODE_SHORT_K 1
+#endif
 // Occupancy the register allocation aims for (waves per SIMD): 4 for one
 // 16-row tile of activation rows (two 8-wave workgroups per CU), 2 for two.
 #ifndef W4_DECODE_WAVES_PER_SIMD
@@ -389,7 +394,9 @@ void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.N / 16) * a.E;
   const int64_t avg = (a.R + a.E - 1) / a.E;   // rows per expert: 16-row MFMA tiles per pass
   const bool deep = tiles < 4096;
-  if (avg <= 16) {
+  if (avg <= 16 && W4_DECODE_SHORT_K && gemm_short_supported(a)) {
+    launch_gemm_short(a, stream);   // K <= 1024: several whole tiles per wave
+  } else if (avg <= 16) {
     if (deep) launch_m<1, 16>(a, stream);
     else launch_m<1, W4_DECODE_RING>(a, stream);
   } else {

@@ -37,6 +37,8 @@ void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 bool gemm_tiled_supported(const GemmArgs& a);
 size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N);
 void launch_gemm_tiled(const GemmArgs& a, void* ws, hipStream_t stream);
+bool gemm_short_supported(const GemmArgs& a);
+void launch_gemm_short(const GemmArgs& a, hipStream_t stream);
 bool gemm_splitk_supported(const GemmArgs& a);
 size_t gemm_splitk_workspace(int64_t R, int64_t K, int64_t N);
 void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream);

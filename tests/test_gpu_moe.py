@@ -95,6 +95,44 @@ def test_gmm_plain_f32_with_gather(E, R, K, N):
     assert ok and not np.isnan(got).any()
 
 
+# Short-K kernel (K <= 1024, plain epilogue, <= 16 rows per expert on
+# average): an expert above 16 rows takes several row passes; K at the limit
+# (8 full blocks), with 3 tail groups, and below one block; tiles per expert
+# not a multiple of the workgroup's 16; both output types.
+@pytest.mark.parametrize("K,N,counts,out_dtype", [
+    (704, 96, [40, 0, 5, 3], w4.W4_OUT_F32),
+    (1024, 64, [17, 1, 0, 16, 2], w4.W4_OUT_F32),
+    (992, 272, [3, 33, 0, 9], w4.W4_OUT_BF16),
+    (96, 48, [1, 2, 20, 0, 4], w4.W4_OUT_BF16),
+])
+def test_gmm_short_k(K, N, counts, out_dtype):
+    rng = gen.rng_for(932, K + N)
+    E = len(counts)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    x_rows = R // 2 + 3
+    x = gen.bf16_normal(rng, (x_rows, K))
+    row_index = rng.integers(0, x_rows, R).astype(np.int32)
+    packed, sct, codes, sc = expert_weights(rng, E, N, K)
+    say("[gmm short-K] K=%d N=%d counts=%s" % (K, N, counts))
+    tdt = torch.float32 if out_dtype == w4.W4_OUT_F32 else torch.bfloat16
+    out = torch.full((R, N), float("nan"), dtype=tdt, device="cuda")
+    w4.moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
+               w4.W4_EPI_NONE, out, out_dtype)
+    torch.cuda.synchronize()
+    got = (out.cpu().numpy().astype(np.float64) if out_dtype == w4.W4_OUT_F32
+           else oracle.bf16_bits_to_f64(bits_host(out)))
+    ref = np.zeros((R, N))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            ref[lo:hi] = oracle.linear_f64(x[row_index[lo:hi]], codes[e], sc[e])
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok and not np.isnan(got).any()
+
+
 @pytest.mark.parametrize("act", [w4.W4_EPI_GEGLU_TANH, w4.W4_EPI_SWIGLU])
 def test_gmm_gated_epilogue(act):
     E, R, K, N = 6, 90, 256, 128
