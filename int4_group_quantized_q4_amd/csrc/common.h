@@ -54,12 +54,18 @@ __host__ __device__ constexpr int tile16_bit(int i) { return 4 * (i >> 1) + 16 *
 // Offset-binary nibble u of every code in the word -> bf16 pairs (128 + u of
 // code 2d | 128 + u of code 2d+1 << 16), d = 0..3.  0x4300 is bf16 128.0, whose
 // 7 mantissa bits step by 1, so OR-ing u in gives 128 + u = 136 + q exactly.
+// The nibbles are split once into the low and high nibble of every byte
+// (lo: codes 0, 4, 1, 5; hi: codes 2, 6, 3, 7 by byte), and each pair is one
+// byte permute of those bytes against 0x43 (7 VALU ops per word).
 __device__ __forceinline__ u32x4 biased_pairs(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
   u32x4 p;
-  p[0] = (w & 0x000F000Fu) | 0x43004300u;
-  p[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  p[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  p[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  // v_perm_b32(S0, S1, sel): selector bytes 0-3 take S1's bytes, 4-7 S0's
+  p[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04020400u);   // [lo.b0, 43, lo.b2, 43] = codes 0, 1
+  p[1] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04020400u);   // codes 2, 3
+  p[2] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030401u);   // [lo.b1, 43, lo.b3, 43] = codes 4, 5
+  p[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u);   // codes 6, 7
   return p;
 }
 
