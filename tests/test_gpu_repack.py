@@ -119,3 +119,31 @@ def test_dequant_random_weights():
     out = w4.dequant(to_dev(layout.encode(codes)), bf16_dev(layout.encode_scales(sc)), rows, K)
     torch.cuda.synchronize()
     assert f32_bits_equal(out.cpu().numpy(), oracle.dequant_f32(codes, sc))
+
+
+def test_repack_decision_boundaries():
+    """Groups whose quotients sit on the decision boundaries: distances to the
+    nearest integer of exactly 3/32 and a bf16 step either side (groups that
+    are accepted at the boundary), and exact ties of the m = 8 fallback
+    (off-grid groups keep those codes); peaks whose trial steps a/m are
+    inexact (a = 7, 5.5, 3 x 2^k, 1e-3-scale) and tiny and huge magnitudes
+    (the division-only path).  Bit-exact against the oracle."""
+    rng = np.random.default_rng(912)
+    near = np.array([0.0, 3 / 32, -3 / 32, 3 / 32 - 2 ** -9, -(3 / 32 - 2 ** -9), 3 / 32 + 2 ** -9])
+    far = np.array([0.0, 0.5, -0.5, 1.5, 3 / 32 + 2 ** -7, 0.125])
+    groups = []
+    for peak in (8.0, 7.0, 5.5, 3.0, 6.0, 7.0 * 2.0 ** -10, 1e-3 * 7, 2.0 ** -120 * 8, 2.0 ** 110 * 5):
+        for m in range(1, 9):
+            for deltas in (near, near, far):
+                s = peak / m
+                q = rng.integers(-min(m, 8), min(m, 7) + 1, 32).astype(np.float64)
+                q[rng.integers(32)] = m if m < 8 else -8
+                d = rng.choice(deltas, 32) * (rng.random(32) < 0.5)
+                d[np.abs(q) == m] = 0.0
+                groups.append((q + d) * s)
+    w = oracle.bf16_from_f64(np.array(groups))
+    rows = (len(groups) // 16) * 16
+    w = w[:rows].reshape(rows, 32)
+    say("[repack] decision boundaries: %d groups" % rows)
+    ref, _ = run_and_check(w, "decision boundaries")
+    say("  off-grid %d of %d" % (ref["off_grid"], rows))
