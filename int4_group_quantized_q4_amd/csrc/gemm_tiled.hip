@@ -211,22 +211,47 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   const int cnt = (int)(e_end - row_begin < BM ? e_end - row_begin : BM);
 
   // this wave's weight tiles (tile16 tile index inside the expert's matrix)
+  // and its row tiles [mt_lo, mt_hi).  When the column block holds work for
+  // only 1 or 2 waves (the last block of a matrix whose tile count is not a
+  // multiple of the block's), the other waves take the same weight tiles and
+  // the row tiles are split between them instead of idling.
   const int tiles_total = (int)(N / kTileRows);
   int tile[WN_TILES];
-  bool active;
-  if constexpr (GATED) {
-    const int half = tiles_total / 2;
-    const int g0 = nb * (BN_TILES / 2) + wv * 2;   // two gate tiles per wave; half is even
-    active = g0 < half;
-    tile[0] = g0;
-    tile[1] = g0 + 1;
-    tile[2] = g0 + half;
-    tile[3] = g0 + 1 + half;
-  } else {
-    const int t0 = nb * BN_TILES + wv * WN_TILES;
-    active = t0 < tiles_total;                     // tiles_total is a multiple of 4
+  bool active = true;
+  int mt_lo = 0, mt_hi = MT;
+  {
+    const int per_wave = GATED ? 2 : WN_TILES;   // gate tiles (gated) or tiles per wave
+    const int left = GATED ? tiles_total / 2 - nb * (BN_TILES / 2) : tiles_total - nb * BN_TILES;
+    const int nact = left / per_wave < NWAVES ? left / per_wave : NWAVES;   // left % per_wave == 0
+    int src = wv;
+    if (nact > 0 && nact < NWAVES && NWAVES % nact == 0) {
+      const int parts = NWAVES / nact;
+      src = wv % nact;
+      mt_lo = (wv / nact) * (MT / parts);
+      mt_hi = mt_lo + MT / parts;
+    } else {
+      active = wv < nact;
+    }
+    if constexpr (GATED) {
+      const int half = tiles_total / 2;
+      const int g0 = nb * (BN_TILES / 2) + src * 2;   // two gate tiles per wave; half is even
+      tile[0] = g0;
+      tile[1] = g0 + 1;
+      tile[2] = g0 + half;
+      tile[3] = g0 + 1 + half;
+    } else {
+      const int t0 = nb * BN_TILES + src * WN_TILES;   // tiles_total is a multiple of 4
 #pragma unroll
-    for (int t = 0; t < WN_TILES; ++t) tile[t] = t0 + t;
+      for (int t = 0; t < WN_TILES; ++t) tile[t] = t0 + t;
+    }
+  }
+  // row tiles past the expert's last row are skipped (their MFMAs and operand
+  // reads); all waves still take part in the staging and the barriers
+  {
+    const int nmt = (cnt + 15) >> 4;
+    mt_hi = mt_hi < nmt ? mt_hi : nmt;
+    mt_lo = __builtin_amdgcn_readfirstlane(mt_lo);
+    mt_hi = __builtin_amdgcn_readfirstlane(mt_hi);
   }
   if (!active) {
     // idle waves still take part in the staging and the barriers
@@ -366,6 +391,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
+      if (i < mt_lo || i >= mt_hi) continue;   // wave-uniform
       const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
       for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A, B[t], acc[i][t]);
@@ -464,6 +490,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         const int apos = jj ? apos1 : apos0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
+          if (i < mt_lo || i >= mt_hi) continue;
           const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
           for (int t = 0; t < WN_TILES; ++t) {
@@ -481,6 +508,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // results are rounded to nearest even by the hardware conversion.
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    if (i < mt_lo || i >= mt_hi) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = 16 * i + 4 * c + q;
