@@ -14,9 +14,10 @@
 // two whole tiles in registers: the next tile's codes and scales are loaded
 // while the current one is multiplied, so only the first tile's latency is
 // exposed.  The expert's activation rows (all of K, at most 16 rows per pass)
-// are staged in LDS once per workgroup.  Per group the partial dot products
-// come out of the matrix core as in the streaming kernel (bf16 128+u codes, a
-// -136 operand for the bias, fp32 scale per group on the VALU).  A tile's
+// are staged in LDS once per workgroup, with a table of -136 x each row's sum
+// over each group.  Per group one MFMA takes the bf16 128+u codes with that
+// table entry as its accumulator input, which cancels the +136 bias; the fp32
+// scale per group is applied on the VALU.  A tile's
 // full-block scales (NBF x 128 B, contiguous) are one 128-bit load per lane,
 // parked in a per-wave LDS buffer (one per register set) before use.
 
@@ -49,6 +50,7 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
   constexpr int CB = NBF > 0 ? NBF : 1;
   __shared__ __align__(16) uint8_t xs[16 * (2 * kMaxCols + 16)];
   __shared__ __align__(16) uint8_t ssc[kSW * 2 * 1024];
+  __shared__ __align__(16) float ctab[(kMaxCols / kGroup) * 16];   // [G][16]: -136 x group sum of each row
 
   const int wg = short_xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
@@ -96,7 +98,6 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
       }
   };
 
-  const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t row0 = row_begin; row0 < row_end; row0 += 16) {
@@ -130,11 +131,29 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
         }
       }
       __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's DMA has landed
+      // bias table of the rows this wave staged: -136 x the row's sum over
+      // each group, lane g for group g
+#pragma unroll
+      for (int h = 0; h < 16 / kSW; ++h) {
+        const int m = wv + kSW * h;
+        if (m < cnt && lane < G) {
+          const uint8_t* xr = xs + m * XS + lane * 64;
+          float sum = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(xr + 16 * v);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sum += bf16_to_f32(q[k] & 0xFFFFu) + bf16_to_f32(q[k] >> 16);
+          }
+          ctab[lane * 16 + m] = -136.f * sum;
+        }
+      }
     }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* xa = xs + arow * XS + c * 16;
+    const uint8_t* ca = reinterpret_cast<const uint8_t*>(ctab) + c * 16;   // rows 4c .. 4c+3
     const uint32_t obase = (uint32_t)(((row0 + 4 * c) * N + r) * ESZ);
     auto run_tile = [&](const u32x4* cw, const uint32_t* ct, const u32x4& sp, const uint32_t* st, int i,
                         int set) __attribute__((always_inline)) {
@@ -148,12 +167,20 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
         const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + 128 * b + 8 * r);
         const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16), bf16_to_f32(sv[1] & 0xFFFFu),
                              bf16_to_f32(sv[1] >> 16)};
+        constexpr int NP = NBF >= 7 ? 1 : 2;   // independent groups at a time (two sets of 7-8 blocks leave room for 1)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (b * 4 + j) * 64);
-          const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
-          const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(cw[b][j])), cb);
-          acc += sc[j] * p;
+        for (int h = 0; h < 4; h += NP) {
+          bf16x8 A[NP];
+          f32x4 p[NP];
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            A[j] = *reinterpret_cast<const bf16x8*>(xa + (b * 4 + h + j) * 64);
+            p[j] = *reinterpret_cast<const f32x4*>(ca + (b * 4 + h + j) * 64);
+          }
+#pragma unroll
+          for (int j = 0; j < NP; ++j) p[j] = mfma16x16x32(A[j], as_bf16x8(biased_pairs(cw[b][h + j])), p[j]);
+#pragma unroll
+          for (int j = 0; j < NP; ++j) acc += sc[h + j] * p[j];
         }
         __builtin_amdgcn_sched_barrier(0);   // one block's operands live at a time
       }
@@ -161,7 +188,7 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
       for (int j = 0; j < 3; ++j)
         if (j < gtail) {
           const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (NBF * 4 + j) * 64);
-          const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+          const f32x4 cb = *reinterpret_cast<const f32x4*>(ca + (NBF * 4 + j) * 64);
           const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(ct[j])), cb);
           acc += bf16_to_f32(st[j]) * p;
         }

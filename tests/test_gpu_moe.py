@@ -133,6 +133,53 @@ def test_gmm_short_k(K, N, counts, out_dtype):
     assert ok and not np.isnan(got).any()
 
 
+# Decode shapes (a few rows per expert) with many weight tiles: the streaming
+# kernel's ring variants (>= 4096 tiles in all, and fewer) and the short-K
+# kernel (K = 736).  Partial last blocks of 1, 2 and 3 groups and whole
+# blocks; plain fp32 / bf16 and both gated outputs; experts with 0, 1, 8, 9
+# and 17 rows (one and two passes of 16).
+@pytest.mark.parametrize("E,N,K,epi,out_dtype", [
+    (16, 8192, 1056, w4.W4_EPI_NONE, w4.W4_OUT_F32),
+    (32, 4096, 736, w4.W4_EPI_NONE, w4.W4_OUT_BF16),
+    (16, 8192, 2848, w4.W4_EPI_SWIGLU, w4.W4_OUT_BF16),
+    (16, 8192, 1024, w4.W4_EPI_GEGLU_TANH, w4.W4_OUT_BF16),
+    (32, 1024, 3040, w4.W4_EPI_NONE, w4.W4_OUT_BF16),
+])
+def test_gmm_decode_many_tiles(E, N, K, epi, out_dtype):
+    counts = ([1, 0, 0, 8, 9, 0, 17, 0, 3] + [0] * E)[:E - 1] + [2]
+    rng = gen.rng_for(933, K + epi + E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    x_rows = R + 5
+    x = gen.bf16_normal(rng, (x_rows, K))
+    row_index = rng.integers(0, x_rows, R).astype(np.int32)
+    packed, sct, codes, sc = expert_weights(rng, E, N, K)
+    say("[gmm decode] E=%d N=%d K=%d epi=%d out=%d" % (E, N, K, epi, out_dtype))
+    gated = epi != w4.W4_EPI_NONE
+    NO = N // 2 if gated else N
+    tdt = torch.float32 if out_dtype == w4.W4_OUT_F32 else torch.bfloat16
+    out = torch.full((R, NO), float("nan"), dtype=tdt, device="cuda")
+    w4.moe_gmm(bf16_dev(x), to_dev(row_index), to_dev(offsets), E, R, K, N, to_dev(packed), bf16_dev(sct),
+               epi, out, out_dtype)
+    torch.cuda.synchronize()
+    got = (out.cpu().numpy().astype(np.float64) if out_dtype == w4.W4_OUT_F32
+           else oracle.bf16_bits_to_f64(bits_host(out)))
+    ref = np.zeros((R, NO))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            if gated:
+                h = oracle.bf16_bits_to_f64(oracle.linear(x[row_index[lo:hi]], codes[e], sc[e]))
+                fn = oracle.gelu_tanh if epi == w4.W4_EPI_GEGLU_TANH else oracle.moe.silu
+                ref[lo:hi] = fn(h[:, :NO]) * h[:, NO:]
+            else:
+                ref[lo:hi] = oracle.linear_f64(x[row_index[lo:hi]], codes[e], sc[e])
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok and not np.isnan(got).any()
+
+
 @pytest.mark.parametrize("act", [w4.W4_EPI_GEGLU_TANH, w4.W4_EPI_SWIGLU])
 def test_gmm_gated_epilogue(act):
     E, R, K, N = 6, 90, 256, 128
