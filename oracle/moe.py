@@ -81,6 +81,23 @@ def route(logits, k):
     }
 
 
+def combine(o, inv, weights):
+    """The weighted combine back into token order: y64[t] = sum over slots j of
+    weights[t, j] * o[inv[t*k + j]], in fp64.
+
+    o        float64 [R, d]   expert outputs, indexed by sorted position
+    inv      int    [T*k]     sorted position of routed row t*k + j
+    weights  float  [T, k]    the top-k softmax weights
+    """
+    T, k = weights.shape
+    inv = np.asarray(inv).reshape(T, k)
+    w = np.asarray(weights, dtype=np.float64)
+    y64 = np.zeros((T, o.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y64 = y64 + w[:, j:j + 1] * o[inv[:, j]]
+    return y64
+
+
 def moe_layer(x_bits, logits, w1_codes, w1_scale, w2_codes, w2_scale, k=8,
               activation="gelu_tanh", keep=False):
     """One MoE layer.
@@ -120,11 +137,7 @@ def moe_layer(x_bits, logits, w1_codes, w1_scale, w2_codes, w2_scale, k=8,
         if keep:
             h_all[lo:hi] = h_bits
             a_all[lo:hi] = a_bits
-    w = plan["weights"]
-    inv = plan["inv"].reshape(T, k)
-    y64 = np.zeros((T, d), dtype=np.float64)
-    for j in range(k):
-        y64 = y64 + w[:, j:j + 1] * o[inv[:, j]]
+    y64 = combine(o, plan["inv"], plan["weights"])
     out = {"y": bf16_from_f64(y64), "y64": y64, "plan": plan}
     if keep:
         out.update(h=h_all, a=a_all, o=o)

@@ -202,6 +202,35 @@ def test_gmm_gated_epilogue(act):
     assert ok
 
 
+# The weighted combine on its own: fp32 and bf16 expert outputs, k a multiple
+# of the kernel's 4-slot chunk (8, 12), below it (1, 3) and between (5).
+@pytest.mark.parametrize("T,k,N,o_dtype", [(64, 8, 2816, w4.W4_OUT_F32), (64, 8, 2816, w4.W4_OUT_BF16),
+                                           (5, 3, 96, w4.W4_OUT_BF16), (33, 1, 64, w4.W4_OUT_F32),
+                                           (7, 5, 16, w4.W4_OUT_F32), (3, 12, 48, w4.W4_OUT_BF16)])
+def test_combine(T, k, N, o_dtype):
+    rng = gen.rng_for(941, T * k + N + o_dtype)
+    R = T * k
+    inv = rng.permutation(R).astype(np.int32)
+    wts = rng.random((T, k)).astype(np.float32)
+    if o_dtype == w4.W4_OUT_F32:
+        o = rng.standard_normal((R, N)).astype(np.float32)
+        o_dev = torch.from_numpy(o).cuda()
+        o64 = o.astype(np.float64)
+    else:
+        o_bits = gen.bf16_normal(rng, (R, N))
+        o_dev = bf16_dev(o_bits)
+        o64 = oracle.bf16_bits_to_f64(o_bits)
+    say("[combine] T=%d k=%d N=%d o_dtype=%d" % (T, k, N, o_dtype))
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_moe_combine(o_dev, o_dtype, to_dev(inv), to_dev(wts), T, k, N, y)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(bits_host(y))
+    ref = oracle.moe.combine(o64, inv, wts)
+    ok, mx, rms = oracle.within_tolerance(got, ref)
+    say("  max_rel %.2e rms_rel %.2e" % (mx, rms))
+    assert ok
+
+
 def moe_inputs(cfg, seed_base=0):
     rng = gen.rng_for(cfg["id"], 20 + seed_base)
     T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
