@@ -52,10 +52,10 @@ EXPERT_W2_BYTES = 2816 * 704 // 2 + 2816 * 22 * 2    # 1,115,136
 TRAFFIC = {
     "decode_gmm1": {"sources": ("gemm_skinny.hip", "common.h", "internal.h"),
                     "sha256": "587082ab59337f91c8ccf5c4aed3a782108b7577db97f36e5fe1b4a763bd30ca",
-                    "read_bytes": 289760304, "write_bytes": 720896},
+                    "read_bytes": 289843200, "write_bytes": 720896},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "677d433d14841d1e4f0b095f30bf6738976026afa08477a753b8fb92e2e5a7fa",
-                     "read_bytes": 540806988, "write_bytes": 46152704},
+                     "sha256": "b5f0171d53f59251d5526faf068fb4665bd817546c6658096fb7b1cc257cf283",
+                     "read_bytes": 534571008, "write_bytes": 46158980},
 }
 
 
