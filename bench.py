@@ -14,6 +14,7 @@ Workloads (default: moe-decode, with moe-prefill measured in the same run):
   moe-decode    T=64 tokens, d_model 2816, 128 experts, expert hidden 704, top-8
   moe-prefill   T=4096 tokens, same experts, Zipf(1.1) expert popularity
   dense-decode  w4a16_linear, M in {1, 8, 16}, K=4096, N=14336
+  dense-prefill w4a16_linear, M=4096, K=4096, N=14336 (TFLOP/s)
   repack        q4_group_repack of 30 layers x 128 experts of on-grid bf16 weights
   e2e           repack of the 30 layers, then T=256 decode through all 30 layers
 
@@ -298,6 +299,38 @@ def dense_decode_report(steps, warmup):
     return res
 
 
+def dense_prefill_report(steps, warmup):
+    """w4a16_linear over a 4096-row prompt: 2*M*N*K flops per call against the
+    bf16/fp16 MFMA peak."""
+    dev = torch.device("cuda:0")
+    cfg = gen.DENSE_PREFILL
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    g = gen.torch_generator(dev, 98)
+    copies = 8   # 8 x 33 MB of weights > 256 MB last-level cache
+    qs = [gen.bytes_uniform_t(g, N * K // 2, dev) for _ in range(copies)]
+    ss = [gen.scales_loguniform_t(g, (N, K // 32), dev) for _ in range(copies)]
+    x = gen.bf16_normal_t(g, (M, K), dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
+    for i in range(warmup):
+        w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 2.0 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "dense-prefill: w4a16_linear M=%d K=%d N=%d" % (M, K, N), "us_per_call": ms * 1e3,
+            "TFLOPs": tf, "flops_per_call": flops,
+            "roofline": {"bound": "mfma", "kernel": "w4a16_linear (prefill GEMM, fp16 MFMA on exact s*q)",
+                         "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                         "traffic": None}}
+
+
 # ------------------------------------------------------------------- repack
 def repack_layers(layers, dev, gen_seed=5):
     """Generate each layer's on-grid bf16 source on the device, repack it and
@@ -400,7 +433,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="moe-decode",
-                    choices=["moe-decode", "moe-prefill", "dense-decode", "repack", "e2e", "copy"])
+                    choices=["moe-decode", "moe-prefill", "dense-decode", "dense-prefill", "repack", "e2e", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
@@ -443,6 +476,11 @@ def main():
                      "dtype": "bf16 x int4 (fp32 accumulate)",
                      "config": {"workload": "dense-decode: w4a16_linear K=4096 N=14336, M in {1,8,16}"},
                      "dense": res})
+    elif args.workload == "dense-prefill":
+        res = dense_prefill_report(args.steps, args.warmup)
+        line.update({"value": res["TFLOPs"], "unit": "TFLOP/s", "ms_per_step": res["us_per_call"] / 1e3,
+                     "dtype": "bf16 x int4 (fp32 accumulate)", "config": {"workload": res.pop("workload")},
+                     "roofline": res.pop("roofline"), "dense": res})
     elif args.workload == "repack":
         res = repack_report()
         line.update({"value": res["groups_per_s"], "unit": "groups/s", "ms_per_step": res["repack_s"] * 1e3,

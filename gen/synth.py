@@ -5,6 +5,7 @@ Distributions and shapes of the five workloads:
   dense-tiny     M=4, K=256, N=512, group 32; plus an on-grid bf16 repack
                  source whose per-group peak level is uniform in 1..8.
   dense-decode   M in {1, 8, 16}, K=4096, N=14336.
+  dense-prefill  M=4096, K=4096, N=14336 (the same projection over a prompt).
   moe-decode     T=64 tokens, d_model=2816, 128 experts, expert hidden 704
                  (fused gate/up 2816 -> 2x704, down 704 -> 2816), top-8,
                  router logits N(0,1).
@@ -30,6 +31,7 @@ GROUP = 32
 
 DENSE_TINY = dict(id=1, M=4, K=256, N=512, peak=(1, 8))
 DENSE_DECODE = dict(id=2, Ms=(1, 8, 16), K=4096, N=14336)
+DENSE_PREFILL = dict(id=6, M=4096, K=4096, N=14336)
 MOE_DECODE = dict(id=3, T=64, d=2816, I=704, E=128, k=8, router="normal")
 MOE_PREFILL = dict(id=4, T=4096, d=2816, I=704, E=128, k=8, router="zipf", zipf_s=1.1)
 MOE_E2E = dict(id=5, layers=30, T=256, d=2816, I=704, E=128, k=8, router="normal", peak=(4, 8))

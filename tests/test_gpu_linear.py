@@ -43,6 +43,31 @@ def test_linear_dense_decode_full_size(M):
     check_linear(M, cfg["K"], cfg["N"], 100 + M, "dense-decode M=%d" % M)
 
 
+def test_linear_dense_prefill_full_size():
+    """M = 4096 rows through the prefill (MFMA) kernel; 24 sampled rows, every
+    column, against the oracle (the whole product would take the oracle
+    minutes), plus the row-scale edge: one row 2^20 times larger than the rest
+    and one 2^-20 times smaller."""
+    cfg = gen.DENSE_PREFILL
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    rng = gen.rng_for(921, 1)
+    packed, sct, codes, sc = linear_weights(rng, N, K)
+    x = gen.bf16_normal(rng, (M, K))
+    xs = oracle.bf16_bits_to_f64(x)
+    xs[5] *= 2.0 ** 20
+    xs[M - 2] *= 2.0 ** -20
+    x = oracle.bf16_from_f64(xs)
+    y = run_linear(x, packed, sct, N)
+    rows = np.unique(np.concatenate([[0, 5, M - 2, M - 1], rng.choice(M, 20, replace=False)]))
+    ref = oracle.linear(x[rows], codes, sc)
+    worst = (0.0, 0.0)
+    for i, row in enumerate(rows):   # row by row: the scaled rows would hide the others' errors
+        ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(y[row]), oracle.bf16_bits_to_f64(ref[i]))
+        worst = (max(worst[0], mx), max(worst[1], rms))
+        assert ok, (row, mx, rms)
+    say("  dense-prefill %d rows: worst max_rel %.2e rms_rel %.2e" % (len(rows), worst[0], worst[1]))
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 32, 16), (2, 96, 48), (3, 704, 32), (5, 2816, 64), (17, 256, 128),
                                    (33, 512, 64), (64, 160, 16), (100, 1024, 48), (300, 128, 32)])
 def test_linear_ragged_shapes(M, K, N):
