@@ -160,9 +160,13 @@ def router_logits_t(gen, T, E, device, law="normal", zipf_s=1.1):
     return (logp[None, :] + gumbel).to(torch.float32)
 
 
-def ongrid_source_t(gen, rows, K, peak_lo, peak_hi, device):
+def ongrid_source_t(gen, rows, K, peak_lo, peak_hi, device, export=False):
     """Device version of ``ongrid_source`` (same law, torch RNG).  Returns
-    (w bf16 tensor [rows, K], q0 int8 [rows, K], s0 bf16-bits int16 [rows, G])."""
+    (w bf16 tensor [rows, K], q0 int8 [rows, K], s0 bf16-bits int16 [rows, G]).
+
+    export=True: a "realistic export" instead -- the scale keeps its full fp32
+    precision and w = bf16(s0 * q0) is rounded, as when a QAT model's fp32
+    grid is saved in bf16 (s0 is then returned rounded to bf16)."""
     G = K // GROUP
     L = torch.randint(peak_lo, peak_hi + 1, (rows, G), device=device, generator=gen)
     hi = torch.clamp(L, max=7)
@@ -176,6 +180,7 @@ def ongrid_source_t(gen, rows, K, peak_lo, peak_hi, device):
     q.scatter_(2, pos, peak[..., None])
     uu = torch.rand((rows, G), dtype=torch.float32, device=device, generator=gen)
     s0 = torch.exp(np.log(SCALE_LO) + uu * (np.log(SCALE_HI) - np.log(SCALE_LO)))
-    s0 = (s0.view(torch.int32) & int(np.int32(np.uint32(0xFFF80000).view(np.int32)))).view(torch.float32)
+    if not export:
+        s0 = (s0.view(torch.int32) & int(np.int32(np.uint32(0xFFF80000).view(np.int32)))).view(torch.float32)
     w = (s0[..., None] * q.to(torch.float32)).to(torch.bfloat16).reshape(rows, K)
     return w, q.to(torch.int8).reshape(rows, K), s0.to(torch.bfloat16).view(torch.int16)

@@ -234,3 +234,26 @@ def test_realistic_variant_report():
           % (100 * ident, worst, r["off_grid"]))
     assert r["off_grid"] < G * 0.01
     assert ident > 0.5 and worst < 0.05
+
+
+def test_per_channel_requantization_is_lossy():
+    """Negative control ([RQ] "What changed in vLLM's TPU backend": the default
+    path re-quantizes with one scale per output channel, which would discard
+    the trained grid).  On on-grid g32 weights the group repack reproduces
+    every value, while the symmetric int4 rule with one scale per row
+    (max|row| / 7) changes most of them by a large relative amount."""
+    rng = gen.rng_for(900, 7)
+    rows, K = 64, 2816
+    src = gen.ongrid_source(rng, rows, K, 4, 8)
+    w = oracle.bf16_bits_to_f64(src["w_bits"])
+    r = oracle.repack_groups(src["w_bits"].reshape(-1, 32))
+    deq = oracle.dequant_f32(r["codes"], r["scale"][:, None]).astype(np.float64).reshape(rows, K)
+    assert r["off_grid"] == 0 and np.array_equal(deq, w)
+    q, step = oracle.textbook_quantize(w.astype(np.float32), 7)   # scope: the whole row
+    pc = q.astype(np.float64) * step.astype(np.float64)
+    nz = w != 0
+    rel = np.abs(pc[nz] - w[nz]) / np.abs(w[nz])
+    changed = np.mean(pc != w)
+    print("per-channel control: %.1f%% of values changed, median rel err %.2e, worst %.2e"
+          % (100 * changed, np.median(rel), np.max(rel)))
+    assert changed > 0.5 and np.median(rel) > 0.05
