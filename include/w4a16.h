@@ -173,10 +173,14 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
 
 /*
  * Products and accumulation of w4a16_linear and w4a16_moe_gmm.  Every product
- * x * (s * q) is formed exactly and accumulated in fp32; only the order of the
- * fp32 additions differs between the two kernels:
- *   streaming kernel  bf16 MFMA on q, each 32-group's fp32 partial sum times
- *                     its scale (decode shapes);
+ * of an activation and a code is formed exactly and accumulated in fp32; the
+ * kernels differ in the order of the fp32 additions and in how the scale and
+ * the code offset enter:
+ *   streaming kernels (decode shapes, including the short-K and split-K ones)
+ *                     bf16 MFMA on the codes as 136 + q (exact in bf16), the
+ *                     offset removed through the MFMA's accumulator input
+ *                     (-136 times the activations' fp32 group sum), each
+ *                     32-group's fp32 partial sum times its scale;
  *   tiled kernel      fp16 MFMA on s*q, exact in fp16 for |s| in [2^-14, 2^13),
  *                     with the activation rows converted to fp16 under a
  *                     per-row power of two (exact for every value within 2^32
