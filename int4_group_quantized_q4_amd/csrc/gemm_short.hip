@@ -55,12 +55,6 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
   const int wg = short_xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
   const int wgi = wg - e * wg_per_expert;
-  int64_t row_begin = 0, row_end = a.R;
-  if (a.offsets) {
-    row_begin = a.offsets[e];
-    row_end = a.offsets[e + 1];
-  }
-  if (row_begin >= row_end) return;   // the whole workgroup leaves together
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -74,9 +68,6 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.qweight + (int64_t)e * (N * K / 2)), 0, (int)(N * K / 2), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
-  // the output up to the expert's last row (R * N * ESZ < 2^31, checked on the host)
-  constexpr int ESZ = OUT == W4_OUT_F32 ? 4 : 2;
-  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(row_end * N * ESZ), kRsrcFlags);
 
   // tile of iteration i; past the expert's last tile the loads re-read it
   // and nothing is computed or stored
@@ -98,17 +89,32 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
       }
   };
 
+  // The first pass's first tile does not depend on the expert's rows: its
+  // loads go out before the row range is read, so the weight stream starts
+  // without waiting for that read.
+  u32x4 cwA[CB], cwB[CB], spA = {0u, 0u, 0u, 0u}, spB = {0u, 0u, 0u, 0u};
+  uint32_t ctA[3] = {0u, 0u, 0u}, ctB[3] = {0u, 0u, 0u}, stA[3] = {0u, 0u, 0u}, stB[3] = {0u, 0u, 0u};
+  load_tile(cwA, ctA, spA, stA, 0);
+
+  int64_t row_begin = 0, row_end = a.R;
+  if (a.offsets) {
+    row_begin = a.offsets[e];
+    row_end = a.offsets[e + 1];
+  }
+  if (row_begin >= row_end) {   // the whole workgroup leaves together
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  // the output up to the expert's last row (R * N * ESZ < 2^31, checked on the host)
+  constexpr int ESZ = OUT == W4_OUT_F32 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(row_end * N * ESZ), kRsrcFlags);
+
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t row0 = row_begin; row0 < row_end; row0 += 16) {
+  for (int64_t row0 = row_begin;;) {
     const int cnt = (int)(row_end - row0 < 16 ? row_end - row0 : 16);
     const int arow = r < cnt ? r : 0;   // rows past the count read row 0; never stored
 
-    u32x4 cwA[CB], cwB[CB], spA = {0u, 0u, 0u, 0u}, spB = {0u, 0u, 0u, 0u};
-    uint32_t ctA[3] = {0u, 0u, 0u}, ctB[3] = {0u, 0u, 0u}, stA[3] = {0u, 0u, 0u}, stB[3] = {0u, 0u, 0u};
-
-    __syncthreads();   // the previous pass is done with the staged rows
-    load_tile(cwA, ctA, spA, stA, 0);
     // the pass's activation rows, all of K, by DMA to LDS: wave w copies rows
     // w, w + kSW, ..., 1 KiB (64 lanes x 16 B) per instruction; lanes past K
     // re-read the row's last 16 bytes into the row's own padding (the row
@@ -214,6 +220,10 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
         run_tile(cwB, ctB, spB, stB, i + 1, 1);
       }
     }
+    row0 += 16;
+    if (row0 >= row_end) break;
+    __syncthreads();   // the pass is done with the staged rows
+    load_tile(cwA, ctA, spA, stA, 0);   // the next pass's first tile
   }
 }
 
