@@ -50,20 +50,19 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int V>
+using I = std::integral_constant<int, V>;
 
 constexpr int BM = 128;                      // activation rows per block
 constexpr int WN_TILES = 4;                  // 16-row weight tiles per wave
 #ifndef W4_TILED_WAVES
 #define W4_TILED_WAVES 4
 #endif
-#ifndef W4_TILED_NST
-#define W4_TILED_NST 4
-#endif
 constexpr int NWAVES = W4_TILED_WAVES;       // 2 per SIMD
 constexpr int BN_TILES = NWAVES * WN_TILES;  // weight tiles per block
 constexpr int MT = BM / 16;                  // MFMA row tiles per wave
 constexpr int BK = 64;                       // K per stage: 2 groups
-constexpr int NST = W4_TILED_NST;            // LDS ring depth (activation stages)
+constexpr int NST = 4;                       // LDS ring depth (activation stages)
 constexpr int AROW = BK * 2;                 // bytes of one staged activation row
 constexpr int ASTAGE = BM * AROW;            // 16 KB per stage
 constexpr int AQ = ASTAGE / (1024 * NWAVES); // DMA instructions per wave per stage
@@ -188,7 +187,21 @@ template <int EPI, int OUT, bool EXACT>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(W4_TILED_WPE)))
 tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
-  __shared__ __align__(16) uint8_t As[NST * ASTAGE];
+  // One array per ring slot, every access naming its slot at compile time: the
+  // compiler then tells the slots apart and waits, before an operand read, only
+  // for the DMA that filled that slot, not for the DMAs issued after it.
+  __shared__ __align__(16) uint8_t As0[ASTAGE];
+  __shared__ __align__(16) uint8_t As1[ASTAGE];
+  __shared__ __align__(16) uint8_t As2[ASTAGE];
+  __shared__ __align__(16) uint8_t As3[ASTAGE];
+  static_assert(NST == 4, "one array per ring slot");
+  auto slot_buf = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int j = decltype(J)::value % NST;
+    if constexpr (j == 0) return As0;
+    else if constexpr (j == 1) return As1;
+    else if constexpr (j == 2) return As2;
+    else return As3;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -210,51 +223,34 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   const int64_t row_begin = e_begin + (int64_t)mt * BM;
   const int cnt = (int)(e_end - row_begin < BM ? e_end - row_begin : BM);
 
-  // this wave's weight tiles (tile16 tile index inside the expert's matrix)
-  // and its row tiles [mt_lo, mt_hi).  When the column block holds work for
-  // only 1 or 2 waves (the last block of a matrix whose tile count is not a
-  // multiple of the block's), the other waves take the same weight tiles and
-  // the row tiles are split between them instead of idling.
+  // this wave's weight tiles (tile16 tile index inside the expert's matrix);
+  // in the last column block of a matrix whose tile count is not a multiple of
+  // the block's, waves without tiles only take part in the staging and the
+  // barriers
   const int tiles_total = (int)(N / kTileRows);
   int tile[WN_TILES];
-  bool active = true;
-  int mt_lo = 0, mt_hi = MT;
+  bool active;
   {
     const int per_wave = GATED ? 2 : WN_TILES;   // gate tiles (gated) or tiles per wave
     const int left = GATED ? tiles_total / 2 - nb * (BN_TILES / 2) : tiles_total - nb * BN_TILES;
-    const int nact = left / per_wave < NWAVES ? left / per_wave : NWAVES;   // left % per_wave == 0
-    int src = wv;
-    if (nact > 0 && nact < NWAVES && NWAVES % nact == 0) {
-      const int parts = NWAVES / nact;
-      src = wv % nact;
-      mt_lo = (wv / nact) * (MT / parts);
-      mt_hi = mt_lo + MT / parts;
-    } else {
-      active = wv < nact;
-    }
+    active = wv < left / per_wave;   // left % per_wave == 0
     if constexpr (GATED) {
       const int half = tiles_total / 2;
-      const int g0 = nb * (BN_TILES / 2) + src * 2;   // two gate tiles per wave; half is even
+      const int g0 = nb * (BN_TILES / 2) + wv * 2;   // two gate tiles per wave; half is even
       tile[0] = g0;
       tile[1] = g0 + 1;
       tile[2] = g0 + half;
       tile[3] = g0 + 1 + half;
     } else {
-      const int t0 = nb * BN_TILES + src * WN_TILES;   // tiles_total is a multiple of 4
+      const int t0 = nb * BN_TILES + wv * WN_TILES;   // tiles_total is a multiple of 4
 #pragma unroll
       for (int t = 0; t < WN_TILES; ++t) tile[t] = t0 + t;
     }
   }
-  // row tiles past the expert's last row are skipped (their MFMAs and operand
-  // reads); all waves still take part in the staging and the barriers
-  {
-    const int nmt = (cnt + 15) >> 4;
-    mt_hi = mt_hi < nmt ? mt_hi : nmt;
-    mt_lo = __builtin_amdgcn_readfirstlane(mt_lo);
-    mt_hi = __builtin_amdgcn_readfirstlane(mt_hi);
-  }
+  // row tiles holding rows of the expert (the exact path and the epilogue skip
+  // the others)
+  const int nmt = __builtin_amdgcn_readfirstlane((cnt + 15) >> 4);
   if (!active) {
-    // idle waves still take part in the staging and the barriers
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) tile[t] = 0;
   }
@@ -296,9 +292,9 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     aoff[q] = (uint32_t)(src * K * 2) + (uint32_t)(ch * 16);
     ahigh |= (ch >= 4 ? 1u : 0u) << q;
   }
-  // activations of stage `st` into the buffer of stage `slot_st`
-  auto a_issue = [&](int st, int slot_st) __attribute__((always_inline)) {
-    uint8_t* dst = As + (slot_st % NST) * ASTAGE + (AQ * wv) * 1024;
+  // activations of stage `st` into ring slot J
+  auto a_issue = [&](int st, auto J) __attribute__((always_inline)) {
+    uint8_t* dst = slot_buf(J) + (AQ * wv) * 1024;
     // a one-group last stage re-reads chunks 0..3 in place of 4..7 (unused)
     const bool one = 2 * st + 1 >= G;
 #pragma unroll
@@ -389,9 +385,10 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         B[t][2 * d + 1] = q2[1];
       }
     }
+    // every row tile, also those past the expert's count (never stored):
+    // straight-line code lets the operand reads run ahead of the MFMAs
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      if (i < mt_lo || i >= mt_hi) continue;   // wave-uniform
       const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
       for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A, B[t], acc[i][t]);
@@ -411,17 +408,18 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // The barrier then makes every wave's DMA visible and frees buffer s % NST,
   // which the next stage's DMA refills.
   const int last_st = S - 1;
-  auto stage = [&](int s, auto SLOT, auto HALF) __attribute__((always_inline)) {
+  auto stage = [&](int s, auto SLOT, auto HALF, auto RING) __attribute__((always_inline)) {
     constexpr int sl = decltype(SLOT)::value;
     constexpr int h = decltype(HALF)::value;
+    constexpr int j = decltype(RING)::value;   // s % NST
     const int nb = (s >> 1) + 1;
     const int nbc = nb < NB ? nb : NB - 1;
     if constexpr (h == 0) bblk_issue(nbc, std::integral_constant<int, sl ^ 1>{});
-    a_issue(s + NST - 1 <= last_st ? s + NST - 1 : last_st, s + NST - 1);
+    a_issue(s + NST - 1 <= last_st ? s + NST - 1 : last_st, std::integral_constant<int, j + NST - 1>{});
     // keep the loads at the top of the stage: sunk to its end they would be
     // waited for at once
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* Ab = As + (s % NST) * ASTAGE;
+    const uint8_t* Ab = slot_buf(RING);
     if constexpr (h == 0) block_scales(s >> 1, SLOT);
     fast_group(Ab, apos0, SLOT, std::integral_constant<int, 2 * h>{});
     if (2 * s + 1 < G) fast_group(Ab, apos1, SLOT, std::integral_constant<int, 2 * h + 1>{});
@@ -433,22 +431,23 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   if constexpr (!EXACT) {
     // prologue: block 0, then A(0) .. A(NST-2); wait for A(0) and block 0
     bblk_issue(0, std::integral_constant<int, 0>{});
-#pragma unroll
-    for (int st = 0; st < NST - 1; ++st) a_issue(st <= last_st ? st : last_st, st);
+    a_issue(0, std::integral_constant<int, 0>{});
+    a_issue(1 <= last_st ? 1 : last_st, std::integral_constant<int, 1>{});
+    a_issue(2 <= last_st ? 2 : last_st, std::integral_constant<int, 2>{});
     wait_vm<(NST - 2) * AQ>();
     barrier_only();
 
     int s = 0;
 #pragma unroll 1
     for (; s + 3 < S; s += 4) {
-      stage(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      stage(s + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-      stage(s + 2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
-      stage(s + 3, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+      stage(s, I<0>{}, I<0>{}, I<0>{});
+      stage(s + 1, I<0>{}, I<1>{}, I<1>{});
+      stage(s + 2, I<1>{}, I<0>{}, I<2>{});
+      stage(s + 3, I<1>{}, I<1>{}, I<3>{});
     }
-    if (s < S) stage(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    if (s + 1 < S) stage(s + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    if (s + 2 < S) stage(s + 2, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    if (s < S) stage(s, I<0>{}, I<0>{}, I<0>{});
+    if (s + 1 < S) stage(s + 1, I<0>{}, I<1>{}, I<1>{});
+    if (s + 2 < S) stage(s + 2, I<1>{}, I<0>{}, I<2>{});
     // the loads issued past the end are still in flight: drain before the
     // block's LDS is released
     wait_vm<0>();
@@ -463,11 +462,11 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S; ++s) {
       __syncthreads();
-      a_issue(s, s);
+      a_issue(s, std::integral_constant<int, 0>{});
       bblk_issue(s >> 1, std::integral_constant<int, 0>{});
       wait_vm<0>();
       __syncthreads();
-      const uint8_t* Ab = As + (s % NST) * ASTAGE;
+      const uint8_t* Ab = As0;
       const int ng = (2 * s + 1 < G) ? 2 : 1;
       for (int jj = 0; jj < ng; ++jj) {
         const int g = 2 * (s & 1) + jj;
@@ -490,7 +489,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         const int apos = jj ? apos1 : apos0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          if (i < mt_lo || i >= mt_hi) continue;
+          if (i >= nmt) continue;
           const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
           for (int t = 0; t < WN_TILES; ++t) {
@@ -508,7 +507,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // results are rounded to nearest even by the hardware conversion.
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    if (i < mt_lo || i >= mt_hi) continue;
+    if (i >= nmt) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = 16 * i + 4 * c + q;
