@@ -57,8 +57,11 @@ TRAFFIC = {
                     "sha256": "587082ab59337f91c8ccf5c4aed3a782108b7577db97f36e5fe1b4a763bd30ca",
                     "read_bytes": 289843200, "write_bytes": 720896},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "b5f0171d53f59251d5526faf068fb4665bd817546c6658096fb7b1cc257cf283",
-                     "read_bytes": 534571008, "write_bytes": 46158980},
+                     "sha256": "4149931c886f0be788a5af5e6593bde80c9516577db858d30127774e074bec06",
+                     "read_bytes": 562426470, "write_bytes": 46152806},
+    "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
+                      "sha256": "4149931c886f0be788a5af5e6593bde80c9516577db858d30127774e074bec06",
+                      "read_bytes": 1127654810, "write_bytes": 117454848},
 }
 
 
@@ -330,7 +333,7 @@ def dense_prefill_report(steps, warmup):
             "TFLOPs": tf, "flops_per_call": flops,
             "roofline": {"bound": "mfma", "kernel": "w4a16_linear (prefill GEMM, fp16 MFMA on exact s*q)",
                          "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
-                         "traffic": None}}
+                         "traffic": traffic_of("dense_prefill")}}
 
 
 # ------------------------------------------------------------------- repack
