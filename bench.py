@@ -23,7 +23,8 @@ Workloads (default: moe-decode, with moe-prefill measured in the same run):
 Prints ONE JSON line.  value = touched-expert weight bytes per layer / layer
 time (moe-decode); the roofline object is for the dominant kernel (the gate/up
 grouped matmul), timed with HIP events around its launches inside the timed
-region.  cpu_baseline times the CPU oracle (test infrastructure) on a bounded
+region (the only events there: each record costs a few microseconds of stream
+time, so the per-call breakdown comes from an instrumented pass afterwards).  cpu_baseline times the CPU oracle (test infrastructure) on a bounded
 sample of the same workload.
 """
 
@@ -119,24 +120,28 @@ class MoeLayerSet:
         self.gws = torch.empty(max(16, gws), dtype=torch.uint8, device=device)
 
     def step(self, c, ev=None):
+        """One layer.  ev: None, 2 events (around the gate/up GEMM only) or 5
+        (between all four calls); each event record costs a few microseconds
+        of stream time."""
         L = self.layers[c]
         T, d, I, E, k = self.T, self.d, self.I, self.E, self.k
         R = T * k
-        if ev is not None:
+        full = ev is not None and len(ev) == 5
+        if full:
             ev[0].record()
         w4.w4a16_moe_route(L["logits"], k, self.ids, self.wts, self.offs, self.srows, self.stoks, self.r2s, self.rws)
         if ev is not None:
-            ev[1].record()
+            ev[1 if full else 0].record()
         w4.w4a16_moe_gmm(L["x"], self.stoks, self.offs, E, R, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
                          self.act, w4.W4_OUT_BF16, self.gws)
         if ev is not None:
-            ev[2].record()
+            ev[2 if full else 1].record()
         w4.w4a16_moe_gmm(self.act, None, self.offs, E, R, I, d, L["w2q"], L["w2s"], w4.W4_EPI_NONE, self.o,
                          w4.W4_OUT_F32, self.gws)
-        if ev is not None:
+        if full:
             ev[3].record()
         w4.w4a16_moe_combine(self.o, w4.W4_OUT_F32, self.r2s, self.wts, T, k, d, self.y)
-        if ev is not None:
+        if full:
             ev[4].record()
 
     def touched(self, c):
@@ -147,13 +152,37 @@ class MoeLayerSet:
         return int(np.count_nonzero(counts)), counts
 
 
+WARMUP_MIN_S = 0.3
+
+
+def warm_up(step, warmup):
+    """At least `warmup` untimed steps and at least WARMUP_MIN_S seconds of
+    them: the GPU's clocks reach their sustained level only after a few
+    hundred milliseconds of load (the decode GEMM runs ~10% slower in the
+    first ones)."""
+    import time
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        step(n)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def time_moe(cfg, steps, warmup, copies=3, seed=1234):
+    """Timed region: `steps` layers with HIP events around the gate/up GEMM
+    only (its average launch time, and the whole-layer time).  Afterwards, an
+    instrumented pass with events between all four calls gives the per-call
+    breakdown (route, gate/up, down, combine), whose event records add a few
+    microseconds to each call."""
     dev = torch.device("cuda:0")
     ls = MoeLayerSet(cfg, copies, seed, dev)
     touched = [ls.touched(c)[0] for c in range(copies)]
-    for i in range(warmup):
-        ls.step(i % copies)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    warm_up(lambda i: ls.step(i % copies), warmup)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -162,15 +191,23 @@ def time_moe(cfg, steps, warmup, copies=3, seed=1234):
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # route, gmm1, gmm2, combine
+    g1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    nb = min(steps, 30)
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
+    for i in range(nb):
+        ls.step(i % copies, evb[i])
+    torch.cuda.synchronize()
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evb])  # route, gmm1, gmm2, combine
     mean_touched = float(np.mean([touched[i % copies] for i in range(steps)]))
     return {
         "ms_per_step": total_ms / steps,
+        "gmm1_ms": float(g1.mean()),
+        "gmm1_ms_p10_p90": [float(np.percentile(g1, 10)), float(np.percentile(g1, 90))],
         "route_ms": float(parts[:, 0].mean()),
-        "gmm1_ms": float(parts[:, 1].mean()),
         "gmm2_ms": float(parts[:, 2].mean()),
         "combine_ms": float(parts[:, 3].mean()),
-        "gmm1_ms_p10_p90": [float(np.percentile(parts[:, 1], 10)), float(np.percentile(parts[:, 1], 90))],
+        "instrumented_ms": {k: round(float(parts[:, j].mean()), 5)
+                            for j, k in enumerate(("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms"))},
         "touched_experts": mean_touched,
         "layerset": ls,
     }
@@ -190,6 +227,7 @@ def moe_decode_report(steps, warmup):
         "weight_bytes_per_layer": wbytes,
         "touched_experts": r["touched_experts"],
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "kernel_ms_note": "gmm1 from the timed region; route, gmm2, combine from an instrumented pass after it",
         "roofline": {
             "bound": "hbm",
             "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
@@ -220,6 +258,7 @@ def moe_prefill_report(steps, warmup):
         "ms_per_step": r["ms_per_step"],
         "useful_flops_per_layer": flops1 + flops2,
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "kernel_ms_note": "gmm1 from the timed region; route, gmm2, combine from an instrumented pass after it",
         "roofline": {
             "bound": "mfma",
             "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
@@ -289,9 +328,7 @@ def dense_decode_report(steps, warmup):
         x = gen.bf16_normal_t(g, (M, K), dev)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
-        for i in range(warmup):
-            w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
-        torch.cuda.synchronize()
+        warm_up(lambda i: w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws), warmup)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):
@@ -317,9 +354,7 @@ def dense_prefill_report(steps, warmup):
     x = gen.bf16_normal_t(g, (M, K), dev)
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
-    for i in range(warmup):
-        w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
-    torch.cuda.synchronize()
+    warm_up(lambda i: w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws), warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(steps):
@@ -433,9 +468,7 @@ def e2e_report(steps, warmup):
             x = (x.float() + y.float()).to(torch.bfloat16)   # residual (outside the library)
         return x
 
-    for _ in range(warmup):
-        forward()
-    torch.cuda.synchronize()
+    warm_up(lambda i: forward(), warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -456,9 +489,7 @@ def copy_report(steps, warmup):
     n = 512 << 20
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
     dst = torch.empty(n, dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    warm_up(lambda i: dst.copy_(src), warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
