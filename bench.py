@@ -152,6 +152,51 @@ class MoeLayerSet:
         return int(np.count_nonzero(counts)), counts
 
 
+class TimingEvent:
+    """A HIP event used only for timing, created with hipEventDisableSystemFence:
+    a default event's record ends with a system-scope release (cache writeback
+    and invalidate) that slows the work queued after it by a few microseconds.
+    Recorded on torch's current stream; read only after a device synchronize."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            torch.cuda.init()
+            h = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has loaded
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+
+    def record(self):
+        rc = self._lib().hipEventRecord(self.ev, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 WARMUP_MIN_S = 0.3
 
 
@@ -182,9 +227,9 @@ def time_moe(cfg, steps, warmup, copies=3, seed=1234):
     ls = MoeLayerSet(cfg, copies, seed, dev)
     touched = [ls.touched(c)[0] for c in range(copies)]
     warm_up(lambda i: ls.step(i % copies), warmup)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, stop = TimingEvent(), TimingEvent()
     start.record()
     for i in range(steps):
         ls.step(i % copies, evs[i])
@@ -193,7 +238,7 @@ def time_moe(cfg, steps, warmup, copies=3, seed=1234):
     total_ms = start.elapsed_time(stop)
     g1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
     nb = min(steps, 30)
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
+    evb = [[TimingEvent() for _ in range(5)] for _ in range(nb)]
     for i in range(nb):
         ls.step(i % copies, evb[i])
     torch.cuda.synchronize()
