@@ -374,7 +374,7 @@ def dense_decode_report(steps, warmup):
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
         warm_up(lambda i: w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws), warmup)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         for i in range(steps):
             w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
@@ -400,7 +400,7 @@ def dense_prefill_report(steps, warmup):
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(16, w4.w4a16_linear_workspace(M, K, N)), dtype=torch.uint8, device=dev)
     warm_up(lambda i: w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws), warmup)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = TimingEvent(), TimingEvent()
     a.record()
     for i in range(steps):
         w4.w4a16_linear(x, qs[i % copies], ss[i % copies], N, y, ws)
@@ -436,7 +436,7 @@ def repack_layers(layers, dev, gen_seed=5):
         w2q = torch.empty(E * d * I // 2, dtype=torch.uint8, device=dev)
         w2s = torch.empty(E * d, I // 32, dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         w4.q4_group_repack(w1, w1q, w1s, None, off)
         w4.q4_group_repack(w2, w2q, w2s, None, off)
@@ -465,7 +465,7 @@ def repack_export_report():
         q = torch.empty(rows * K // 2, dtype=torch.uint8, device=dev)
         sc = torch.empty(rows * K // 32, dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         w4.q4_group_repack(w, q, sc, None, off)
         b.record()
@@ -514,7 +514,7 @@ def e2e_report(steps, warmup):
         return x
 
     warm_up(lambda i: forward(), warmup)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = TimingEvent(), TimingEvent()
     a.record()
     for _ in range(steps):
         forward()
@@ -535,7 +535,7 @@ def copy_report(steps, warmup):
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
     dst = torch.empty(n, dtype=torch.uint8, device=dev)
     warm_up(lambda i: dst.copy_(src), warmup)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = TimingEvent(), TimingEvent()
     a.record()
     for _ in range(steps):
         dst.copy_(src)
