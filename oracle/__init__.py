@@ -33,6 +33,13 @@ Parity status of each function (which pins it, see tests/test_oracle_*.py):
                                   built from torch float64 ops; token-order
                                   invariance)
   gelu_tanh                       pinned (torch.nn.functional.gelu tanh, fp64)
+  combine (moe.py)                pinned (one-hot expert rows with distinct
+                                  weights: every slot/weight/token pairing is
+                                  visible; slot order of the fp64 sum)
+  normwise_errors / within_tolerance
+                                  pinned (hand-computed exact vectors that
+                                  separate the normwise figures from element-wise
+                                  or max|y|-based ones; zero and scaled references)
 """
 
 from .bf16 import (

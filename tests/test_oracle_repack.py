@@ -237,11 +237,11 @@ def test_realistic_variant_report():
 
 
 def test_per_channel_requantization_is_lossy():
-    """Negative control ([RQ] "What changed in vLLM's TPU backend": the default
-    path re-quantizes with one scale per output channel, which would discard
-    the trained grid).  On on-grid g32 weights the group repack reproduces
-    every value, while the symmetric int4 rule with one scale per row
-    (max|row| / 7) changes most of them by a large relative amount."""
+    """Negative control for [RQ] "What changed in vLLM's TPU backend": a backend
+    that re-derives int4 with a single scale per output row loses the 32-wide
+    grid the weights were trained on.  On on-grid g32 weights the group repack
+    reproduces every value, while the symmetric int4 rule with one scale per
+    row (max|row| / 7) changes most of them by a large relative amount."""
     rng = gen.rng_for(900, 7)
     rows, K = 64, 2816
     src = gen.ongrid_source(rng, rows, K, 4, 8)
