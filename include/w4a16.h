@@ -145,9 +145,12 @@ int q4_group_repack(const uint16_t* w_bf16, int64_t rows, int64_t K,
 /*
  * q4_group_dequant_f32 -- out[n][k] = fp32(scale[n][k/32]) * q[n][k].
  *
- * [WQ] "How you actually do it" (dequantize = code times scale).  Runs the
- * same in-register nibble unpack as the matmul kernels; the product of an
- * 8-bit and a 4-bit significand is exact in fp32.
+ * [WQ] "How you actually do it" (dequantize = code times scale).  The codes
+ * are unpacked by the routine the weight-streaming matmul kernels (decode,
+ * short-K, split-K) feed to the matrix cores: bf16 136 + q, two codes per
+ * register.  The prefill kernel's fp16 unpack is a different routine, which
+ * this call does not run.  The product of an 8-bit and a 4-bit significand is
+ * exact in fp32.
  *   qweight in rows*K/2 bytes tile16; scales in rows*K/32 tile16; out [rows][K] f32.
  */
 int q4_group_dequant_f32(const uint8_t* qweight, const uint16_t* scales,

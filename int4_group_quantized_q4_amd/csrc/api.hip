@@ -269,6 +269,11 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
   if (I == 0) return W4_ERR_SHAPE;
   if (!x || !logits || !w1_q || !w1_s || !w2_q || !w2_s || !y) return W4_ERR_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < w4a16_moe_layer_workspace(T, E, k, d, I)) return W4_ERR_WORKSPACE;
+  // everything the three later calls check, checked before the first launch
+  // so that an error enqueues nothing
+  if (!aligned16(x) || !aligned16(w1_q) || !aligned16(w1_s) || !aligned16(w2_q) || !aligned16(w2_s) || !aligned16(y))
+    return W4_ERR_ARG;
+  if (2 * I * d / 2 >= ((int64_t)1 << 31) || d * I / 2 >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
   char* base = static_cast<char*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(base + p[0]);
   float* wts = reinterpret_cast<float*>(base + p[1]);

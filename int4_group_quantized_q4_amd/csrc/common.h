@@ -73,55 +73,20 @@ __device__ __forceinline__ u32x4 biased_pairs(uint32_t w) {
 // biased_pairs() through the MFMA's accumulator input.
 constexpr uint32_t kNeg136Pair = 0xC308C308u;
 
-// v_cvt_off_f32_i4 on byte B of a word: the low nibble of that byte, read as a
-// two's-complement 4-bit integer, divided by 16 (exact).  SDWA byte select
-// saves the shift.
-template <int B>
-__device__ __forceinline__ float cvt_i4_byte(uint32_t w) {
-  float r;
-  if constexpr (B == 0) {
-    r = __builtin_amdgcn_cvt_off_f32_i4(w);
-  } else if constexpr (B == 1) {
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
-  } else if constexpr (B == 2) {
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
-  } else {
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
-  }
-  return r;
-}
-
-// The eight codes of a word as exact bf16 values q/16 (element i = code i).
-// Flipping bit 3 of every nibble turns offset binary into two's complement;
-// v_cvt_off_f32_i4 then gives q/16.  Code i sits in nibble (i/2) + 4*(i%2).
-__device__ __forceinline__ bf16x8 unpack8_div16(uint32_t w) {
-  const uint32_t t = w ^ 0x88888888u;
-  const uint32_t h = t >> 4;
-  bf16x8 r;
-  r[0] = (__bf16)cvt_i4_byte<0>(t);   // nibble 0
-  r[1] = (__bf16)cvt_i4_byte<2>(t);   // nibble 4
-  r[2] = (__bf16)cvt_i4_byte<0>(h);   // nibble 1
-  r[3] = (__bf16)cvt_i4_byte<2>(h);   // nibble 5
-  r[4] = (__bf16)cvt_i4_byte<1>(t);   // nibble 2
-  r[5] = (__bf16)cvt_i4_byte<3>(t);   // nibble 6
-  r[6] = (__bf16)cvt_i4_byte<1>(h);   // nibble 3
-  r[7] = (__bf16)cvt_i4_byte<3>(h);   // nibble 7
-  return r;
-}
-
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Gated activations of the MoE epilogues.  gelu with the tanh approximation,
-// tanh(y) = 1 - 2 / (1 + e^(2y)): the absolute error of the hardware exp and
-// reciprocal (~1e-7) moves 0.5 x (1 + tanh) by ~1e-7 relative, far below the
-// bf16 rounding that follows.
+// Gated activations of the MoE epilogues.  gelu with the tanh approximation:
+// 0.5 x (1 + tanh(y)) = x * sigmoid(2y) = x / (1 + e^(-2y)), y = sqrt(2/pi) (x +
+// 0.044715 x^3).  No term cancels, so the hardware exp and reciprocal (about
+// 1e-7 relative each) give about 3e-7 relative error for every x, in the
+// negative tail too (where 1 + tanh(y) formed by subtraction would lose every
+// digit below x = -5); e^(-2y) = inf at large negative x gives -0.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   const float y = c * (x + 0.044715f * x * x * x);
-  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * y));
-  return 0.5f * x * (1.0f + th);
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * y));
 }
 
 __device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }

@@ -55,10 +55,7 @@ using I = std::integral_constant<int, V>;
 
 constexpr int BM = 128;                      // activation rows per block
 constexpr int WN_TILES = 4;                  // 16-row weight tiles per wave
-#ifndef W4_TILED_WAVES
-#define W4_TILED_WAVES 4
-#endif
-constexpr int NWAVES = W4_TILED_WAVES;       // 2 per SIMD
+constexpr int NWAVES = 4;                    // 2 blocks per CU: 2 waves per SIMD
 constexpr int BN_TILES = NWAVES * WN_TILES;  // weight tiles per block
 constexpr int MT = BM / 16;                  // MFMA row tiles per wave
 constexpr int BK = 64;                       // K per stage: 2 groups
@@ -181,10 +178,7 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
 // next, same grid): only blocks with redo set run, recomputing their tile with
 // B = q in fp16 and each group's fp32 partial sum times its fp32 scale.
 template <int EPI, int OUT, bool EXACT>
-#ifndef W4_TILED_WPE
-#define W4_TILED_WPE 2
-#endif
-__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(W4_TILED_WPE)))
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2)))
 tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   // One array per ring slot, every access naming its slot at compile time: the

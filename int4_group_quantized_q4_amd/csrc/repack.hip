@@ -237,7 +237,10 @@ __global__ void __launch_bounds__(256) repack_kernel(
   }
 }
 
-// One thread per 4-byte word (8 codes): out[n][32g + 8c + i] = scale * q.
+// One thread per 4-byte word (8 codes): out[n][32g + 8c + i] = scale * q.  The
+// codes go through biased_pairs(), the unpack the weight-streaming matmul
+// kernels feed to the matrix cores (bf16 136 + q, two codes per register), so
+// a bit-exact check of this output checks that routine's nibble order too.
 __global__ void __launch_bounds__(256) dequant_kernel(
     const uint8_t* __restrict__ qweight, const uint16_t* __restrict__ scales, int64_t rows,
     int64_t K, float* __restrict__ out) {
@@ -253,19 +256,16 @@ __global__ void __launch_bounds__(256) dequant_kernel(
     const uint32_t word = *reinterpret_cast<const uint32_t*>(
         qweight + tile16_word_offset(n / kTileRows, (int)(n % kTileRows), g, c, K));
     const float s = bf16_to_f32(scales[tile16_scale_index(n / kTileRows, (int)(n % kTileRows), g, G)]);
-    const bf16x8 v = unpack8_div16(word);
-    float4 lo, hi;
-    lo.x = s * ((float)v[0] * 16.0f);
-    lo.y = s * ((float)v[1] * 16.0f);
-    lo.z = s * ((float)v[2] * 16.0f);
-    lo.w = s * ((float)v[3] * 16.0f);
-    hi.x = s * ((float)v[4] * 16.0f);
-    hi.y = s * ((float)v[5] * 16.0f);
-    hi.z = s * ((float)v[6] * 16.0f);
-    hi.w = s * ((float)v[7] * 16.0f);
+    const u32x4 p = biased_pairs(word);   // pair d: codes 2d (low half), 2d + 1 (high half)
+    float v[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      v[2 * d] = s * (bf16_to_f32(p[d] & 0xFFFFu) - 136.0f);
+      v[2 * d + 1] = s * (bf16_to_f32(p[d] >> 16) - 136.0f);
+    }
     float4* dst = reinterpret_cast<float4*>(out + n * K + wk * 8);
-    dst[0] = lo;
-    dst[1] = hi;
+    dst[0] = float4{v[0], v[1], v[2], v[3]};
+    dst[1] = float4{v[4], v[5], v[6], v[7]};
   }
 }
 

@@ -36,6 +36,29 @@ def _ptr(t, name, dtypes=None, nullable=False):
     return t.data_ptr()
 
 
+def _bytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(t, name, nbytes, device=None):
+    """Raise ValueError unless tensor t (if given) holds at least nbytes and
+    lives on `device`.  The library sees only pointers, so an undersized
+    buffer would become an out-of-bounds device access: this check runs
+    before any launch."""
+    if t is None:
+        return
+    if _bytes(t) < nbytes:
+        raise ValueError("%s holds %d bytes, the call needs %d" % (name, _bytes(t), nbytes))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _dims(*vals):
+    for v in vals:
+        if int(v) < 0:
+            raise ValueError("sizes must be non-negative")
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -47,6 +70,11 @@ def _stream(stream):
 # ----------------------------------------------------------------- raw calls
 def q4_group_repack(w, qweight, scales, group_status=None, counters=None, stream=None):
     rows, K = w.shape
+    d = w.device
+    _need(qweight, "qweight", rows * K // 2, d)
+    _need(scales, "scales", rows * K // 32 * 2, d)
+    _need(group_status, "group_status", rows * K // 32, d)
+    _need(counters, "counters", 16, d)
     st = lib().q4_group_repack(
         _ptr(w, "w", _BF16_LIKE), rows, K, _ptr(qweight, "qweight", (torch.uint8,)),
         _ptr(scales, "scales", _BF16_LIKE), _ptr(group_status, "group_status", (torch.uint8,), True),
@@ -55,6 +83,11 @@ def q4_group_repack(w, qweight, scales, group_status=None, counters=None, stream
 
 
 def q4_group_dequant_f32(qweight, scales, rows, K, out, stream=None):
+    _dims(rows, K)
+    d = qweight.device
+    _need(scales, "scales", rows * K // 32 * 2, d)
+    _need(qweight, "qweight", rows * K // 2, d)
+    _need(out, "out", rows * K * 4, d)
     st = lib().q4_group_dequant_f32(
         _ptr(qweight, "qweight", (torch.uint8,)), _ptr(scales, "scales", _BF16_LIKE), rows, K,
         _ptr(out, "out", (torch.float32,)), _stream(stream))
@@ -63,12 +96,16 @@ def q4_group_dequant_f32(qweight, scales, rows, K, out, stream=None):
 
 def q4_pack_codes(codes, qweight, stream=None):
     rows, K = codes.shape
+    _need(qweight, "qweight", rows * K // 2, codes.device)
     st = lib().q4_pack_codes(_ptr(codes, "codes", (torch.int8,)), rows, K,
                              _ptr(qweight, "qweight", (torch.uint8,)), _stream(stream))
     check(st, "q4_pack_codes")
 
 
 def q4_pack_scales(scales, rows, K, scales_tiled, stream=None):
+    _dims(rows, K)
+    _need(scales, "scales", rows * K // 32 * 2)
+    _need(scales_tiled, "scales_tiled", rows * K // 32 * 2, scales.device)
     st = lib().q4_pack_scales(_ptr(scales, "scales", _BF16_LIKE), rows, K,
                               _ptr(scales_tiled, "scales_tiled", _BF16_LIKE), _stream(stream))
     check(st, "q4_pack_scales")
@@ -102,6 +139,12 @@ def w4a16_linear_workspace(M, K, N):
 
 def w4a16_linear(x, qweight, scales, N, y, ws=None, stream=None):
     M, K = x.shape
+    _dims(N)
+    d = x.device
+    _need(qweight, "qweight", N * K // 2, d)
+    _need(scales, "scales", N * K // 32 * 2, d)
+    _need(y, "y", M * N * 2, d)
+    _need(ws, "ws", 0, d)
     wp, wn = _ws(ws)
     st = lib().w4a16_linear(_ptr(x, "x", _BF16_LIKE), M, K, _ptr(qweight, "qweight", (torch.uint8,)),
                             _ptr(scales, "scales", _BF16_LIKE), N, _ptr(y, "y", _BF16_LIKE), wp, wn, _stream(stream))
@@ -116,12 +159,19 @@ def w4a16_moe_route(logits, k, topk_ids, topk_weights, expert_offsets, sorted_ro
                     row_to_sorted, ws, stream=None):
     T, E = logits.shape
     i32 = (torch.int32,)
+    d = logits.device
+    R = T * k
+    for t, name in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"), (sorted_rows, "sorted_rows"),
+                    (sorted_tokens, "sorted_tokens"), (row_to_sorted, "row_to_sorted")):
+        _need(t, name, R * 4, d)
+    _need(expert_offsets, "expert_offsets", (E + 1) * 4, d)
+    _need(ws, "ws", 0, d)
+    wp, wn = _ws(ws)
     st = lib().w4a16_moe_route(
         _ptr(logits, "logits", (torch.float32,)), T, E, k, _ptr(topk_ids, "topk_ids", i32),
         _ptr(topk_weights, "topk_weights", (torch.float32,)), _ptr(expert_offsets, "expert_offsets", i32),
         _ptr(sorted_rows, "sorted_rows", i32), _ptr(sorted_tokens, "sorted_tokens", i32),
-        _ptr(row_to_sorted, "row_to_sorted", i32), _ptr(ws, "ws", None, True), ws.numel() * ws.element_size(),
-        _stream(stream))
+        _ptr(row_to_sorted, "row_to_sorted", i32), wp, wn, _stream(stream))
     check(st, "w4a16_moe_route")
 
 
@@ -131,6 +181,21 @@ def w4a16_moe_gmm_workspace(x_rows, R, E, K, N):
 
 def w4a16_moe_gmm(x, row_index, expert_offsets, E, R, K, N, qweight, scales, epilogue, out, out_dtype,
                   ws=None, stream=None):
+    _dims(E, R, K, N)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [x_rows, K=%d], got %s" % (K, tuple(x.shape)))
+    d = x.device
+    _need(row_index, "row_index", R * 4, d)
+    _need(expert_offsets, "expert_offsets", (E + 1) * 4, d)
+    _need(qweight, "qweight", E * N * K // 2, d)
+    _need(scales, "scales", E * N * K // 32 * 2, d)
+    ncol = N // 2 if epilogue in (W4_EPI_GEGLU_TANH, W4_EPI_SWIGLU) else N
+    if out_dtype == W4_OUT_F32 and out.dtype != torch.float32:
+        raise TypeError("out must be float32 for W4_OUT_F32")
+    if out_dtype == W4_OUT_BF16 and out.dtype not in _BF16_LIKE:
+        raise TypeError("out must be bf16 for W4_OUT_BF16")
+    _need(out, "out", R * ncol * (4 if out_dtype == W4_OUT_F32 else 2), d)
+    _need(ws, "ws", 0, d)
     wp, wn = _ws(ws)
     st = lib().w4a16_moe_gmm(
         _ptr(x, "x", _BF16_LIKE), x.shape[0], _ptr(row_index, "row_index", (torch.int32,), True),
@@ -147,6 +212,16 @@ def moe_gmm(x, row_index, expert_offsets, E, R, K, N, qweight, scales, epilogue,
 
 
 def w4a16_moe_combine(o, o_dtype, row_to_sorted, topk_weights, T, k, N, y, stream=None):
+    _dims(T, k, N)
+    d = o.device
+    if o_dtype == W4_OUT_F32 and o.dtype != torch.float32:
+        raise TypeError("o must be float32 for W4_OUT_F32")
+    if o_dtype == W4_OUT_BF16 and o.dtype not in _BF16_LIKE:
+        raise TypeError("o must be bf16 for W4_OUT_BF16")
+    _need(o, "o", T * k * N * o.element_size(), d)
+    _need(row_to_sorted, "row_to_sorted", T * k * 4, d)
+    _need(topk_weights, "topk_weights", T * k * 4, d)
+    _need(y, "y", T * N * 2, d)
     st = lib().w4a16_moe_combine(
         _ptr(o, "o", (torch.float32,) + _BF16_LIKE), o_dtype, _ptr(row_to_sorted, "row_to_sorted", (torch.int32,)),
         _ptr(topk_weights, "topk_weights", (torch.float32,)), T, k, N, _ptr(y, "y", _BF16_LIKE), _stream(stream))
@@ -166,6 +241,17 @@ def w4a16_moe_layer_plan(T, E, k, d, I):
 def w4a16_moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation, y, ws, stream=None):
     T, d = x.shape
     E = logits.shape[1]
+    _dims(k, I)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError("logits must be [T=%d, E], got %s" % (T, tuple(logits.shape)))
+    dv = x.device
+    _need(logits, "logits", T * E * 4, dv)
+    _need(w1_q, "w1_q", E * 2 * I * d // 2, dv)
+    _need(w1_s, "w1_s", E * 2 * I * d // 32 * 2, dv)
+    _need(w2_q, "w2_q", E * d * I // 2, dv)
+    _need(w2_s, "w2_s", E * d * I // 32 * 2, dv)
+    _need(y, "y", T * d * 2, dv)
+    _need(ws, "ws", w4a16_moe_layer_workspace(T, E, k, d, I), dv)
     st = lib().w4a16_moe_layer(
         _ptr(x, "x", _BF16_LIKE), _ptr(logits, "logits", (torch.float32,)), T, E, k, d, I,
         _ptr(w1_q, "w1_q", (torch.uint8,)), _ptr(w1_s, "w1_s", _BF16_LIKE), _ptr(w2_q, "w2_q", (torch.uint8,)),

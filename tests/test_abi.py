@@ -149,3 +149,56 @@ def test_layout_roundtrip_and_documented_offsets():
     ts = layout.encode_scales(sc)
     assert list(np.nonzero(ts)[0]) == [352 + 320 + 2 + 1]
     assert np.array_equal(layout.decode_scales(ts, 32, 704), sc)
+
+
+def test_python_wrappers_reject_undersized_buffers():
+    """The binding checks every buffer's size against the shapes it passes,
+    before any launch: the library sees pointers only, so an undersized tensor
+    would otherwise become an out-of-bounds device access.  (CPU tensors reach
+    the size check first; a correctly sized CPU tensor would then be refused as
+    not on the device.)"""
+    import torch
+    u8 = lambda n: torch.empty(n, dtype=torch.uint8)
+    bf = lambda *s: torch.empty(*s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.empty(*s, dtype=torch.float32)
+    i32 = lambda n: torch.empty(n, dtype=torch.int32)
+    size_err = pytest.raises(ValueError, match="holds .* bytes")
+    with size_err:
+        w4.q4_group_repack(bf(32, 64), u8(32 * 64 // 2 - 1), bf(64))
+    with size_err:
+        w4.q4_group_repack(bf(32, 64), u8(32 * 32), bf(63))
+    with size_err:
+        w4.q4_group_dequant_f32(u8(1024), bf(64), 32, 64, f32(32 * 64 - 1))
+    with size_err:
+        w4.w4a16_linear(bf(4, 256), u8(512 * 128), bf(512 * 8), 512, bf(4, 511))
+    with size_err:
+        w4.w4a16_linear(bf(4, 256), u8(512 * 128 - 16), bf(512 * 8), 512, bf(4, 512))
+    with size_err:
+        w4.w4a16_moe_route(f32(64, 128), 8, i32(512), f32(512), i32(128), i32(512), i32(512), i32(512), u8(1 << 16))
+    E, R, K, N = 4, 40, 256, 128
+    gmm = dict(x=bf(10, K), row_index=i32(R), expert_offsets=i32(E + 1), E=E, R=R, K=K, N=N,
+               qweight=u8(E * N * K // 2), scales=bf(E * N * K // 32), epilogue=w4.W4_EPI_NONE,
+               out=f32(R, N), out_dtype=w4.W4_OUT_F32)
+    for key, bad in (("row_index", i32(R - 1)), ("expert_offsets", i32(E)), ("qweight", u8(E * N * K // 2 - 1)),
+                     ("scales", bf(E * N * K // 32 - 1)), ("out", f32(R, N - 1))):
+        with size_err:
+            w4.w4a16_moe_gmm(**dict(gmm, **{key: bad}))
+    with pytest.raises(ValueError, match="x must be"):
+        w4.w4a16_moe_gmm(**dict(gmm, x=bf(10, K + 32)))
+    with pytest.raises(TypeError):
+        w4.w4a16_moe_gmm(**dict(gmm, out=bf(R, N)))
+    with size_err:   # gated: out has N/2 columns
+        w4.w4a16_moe_gmm(**dict(gmm, epilogue=w4.W4_EPI_GEGLU_TANH, out=bf(R, N // 2 - 1), out_dtype=w4.W4_OUT_BF16))
+    with size_err:
+        w4.w4a16_moe_combine(f32(8 * 2, 64), w4.W4_OUT_F32, i32(16), f32(16), 8, 2, 64, bf(8, 63))
+    with size_err:
+        w4.w4a16_moe_combine(f32(8 * 2 - 1, 64), w4.W4_OUT_F32, i32(16), f32(16), 8, 2, 64, bf(8, 64))
+    T, E, k, d, I = 8, 16, 2, 64, 32
+    need = w4.w4a16_moe_layer_workspace(T, E, k, d, I)
+    layer = dict(x=bf(T, d), logits=f32(T, E), k=k, I=I, w1_q=u8(E * 2 * I * d // 2), w1_s=bf(E * 2 * I * d // 32),
+                 w2_q=u8(E * d * I // 2), w2_s=bf(E * d * I // 32), activation=w4.W4_EPI_GEGLU_TANH, y=bf(T, d),
+                 ws=u8(need))
+    for key, bad in (("w1_q", u8(E * 2 * I * d // 2 - 1)), ("w2_s", bf(E * d * I // 32 - 1)), ("y", bf(T, d - 1)),
+                     ("ws", u8(need - 1))):
+        with size_err:
+            w4.w4a16_moe_layer(**dict(layer, **{key: bad}))
