@@ -323,6 +323,28 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
  */
 int w4a16_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[9]);
 
+/*
+ * w4a16_moe_layer_noalloc -- w4a16_moe_layer without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The workspace is a
+ * static device array of W4_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call itself allocates and frees nothing.  Arguments, outputs and errors are
+ * those of w4a16_moe_layer, plus:
+ *   W4_ERR_WORKSPACE  when w4a16_moe_layer_workspace(T, E, k, d, I) exceeds the
+ *                     array (at d = 2816, I = 704, E = 128, k = 8: T up to 290);
+ *                     nothing is enqueued.
+ *   W4_ERR_HIP        when the array's device address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array and it keeps the last call's
+ * contents (nothing in it needs to start at zero), so calls that overlap on
+ * one GPU -- on two streams, or from two host threads -- race and give wrong
+ * results: serialise them.
+ */
+#define W4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int w4a16_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d,
+                            int64_t I, const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q,
+                            const uint16_t* w2_s, int32_t activation, uint16_t* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

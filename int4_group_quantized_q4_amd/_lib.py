@@ -29,6 +29,8 @@ W4_KERNEL_STREAM = 1
 W4_KERNEL_TILED = 2
 W4_TILED_MIN_ROWS = 64
 
+W4_NOALLOC_SCRATCH_BYTES = 32 << 20
+
 W4_GROUP_OFF_GRID = 0
 W4_GROUP_NONFINITE = 255
 
@@ -57,6 +59,7 @@ SIGNATURES = {
     "w4a16_moe_layer_workspace": (_sz, [_i64, _i32, _i32, _i64, _i64]),
     "w4a16_moe_layer_plan": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64, ctypes.POINTER(_sz)]),
     "w4a16_moe_layer": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz, _p]),
+    "w4a16_moe_layer_noalloc": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p]),
 }
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 #include "w4a16.h"
@@ -256,24 +257,38 @@ size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int
   return layer_gemm_ws_offset(p, T, k, d) + layer_gemm_ws_bytes(T, E, k, d, I);
 }
 
-int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
-                    const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q, const uint16_t* w2_s,
-                    int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Host checks of a layer call, everything but the workspace: W4_OK to run,
+// kLayerEmpty when there is nothing to enqueue, else the error.
+static constexpr int kLayerEmpty = 1;
+static int check_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                       const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                       int32_t activation, const uint16_t* y) {
   if (activation != W4_EPI_GEGLU_TANH && activation != W4_EPI_SWIGLU) return W4_ERR_ARG;
   size_t p[9];
-  int st = w4a16_moe_layer_plan(T, E, k, d, I, p);
+  const int st = w4a16_moe_layer_plan(T, E, k, d, I, p);
   if (st != W4_OK) return st;
   if (d % 32 != 0 || I % 32 != 0) return W4_ERR_SHAPE;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
-  if (T == 0 || d == 0) return W4_OK;
+  if (T == 0 || d == 0) return kLayerEmpty;
   if (I == 0) return W4_ERR_SHAPE;
   if (!x || !logits || !w1_q || !w1_s || !w2_q || !w2_s || !y) return W4_ERR_ARG;
-  if (!ws || !aligned16(ws) || ws_bytes < w4a16_moe_layer_workspace(T, E, k, d, I)) return W4_ERR_WORKSPACE;
-  // everything the three later calls check, checked before the first launch
-  // so that an error enqueues nothing
+  // everything the later calls check, checked before the first launch so that
+  // an error enqueues nothing
   if (!aligned16(x) || !aligned16(w1_q) || !aligned16(w1_s) || !aligned16(w2_q) || !aligned16(w2_s) || !aligned16(y))
     return W4_ERR_ARG;
   if (2 * I * d / 2 >= ((int64_t)1 << 31) || d * I / 2 >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
+int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                    const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q, const uint16_t* w2_s,
+                    int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_layer(x, logits, T, E, k, d, I, w1_q, w1_s, w2_q, w2_s, activation, y);
+  if (st == kLayerEmpty) return W4_OK;
+  if (st != W4_OK) return st;
+  if (!ws || !aligned16(ws) || ws_bytes < w4a16_moe_layer_workspace(T, E, k, d, I)) return W4_ERR_WORKSPACE;
+  size_t p[9];
+  w4a16_moe_layer_plan(T, E, k, d, I, p);
   char* base = static_cast<char*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(base + p[0]);
   float* wts = reinterpret_cast<float*>(base + p[1]);
@@ -296,6 +311,59 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
                      stream);
   if (st != W4_OK) return st;
   return w4a16_moe_combine(o, W4_OUT_F32, r2s, wts, T, k, d, y, stream);
+}
+
+// ---------------------------------------------------------------------------
+// w4a16_moe_layer_noalloc: the layer with its workspace in a static device
+// array instead of a caller buffer.  `scratch` below is a host-side stand-in
+// for that array: its device address on each GPU comes from
+// hipGetSymbolAddress (taken once per device, with that device current) and
+// only that address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[W4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up on first use.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return W4_ERR_HIP;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return W4_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return W4_OK;
+}
+}  // namespace
+
+int w4a16_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d,
+                            int64_t I, const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q,
+                            const uint16_t* w2_s, int32_t activation, uint16_t* y, hipStream_t stream) {
+  const int st = check_layer(x, logits, T, E, k, d, I, w1_q, w1_s, w2_q, w2_s, activation, y);
+  if (st == kLayerEmpty) return W4_OK;
+  if (st != W4_OK) return st;
+  // nothing in the layer's workspace has to start at zero: every kernel writes
+  // what a later one reads, so the array's previous contents never matter
+  if (w4a16_moe_layer_workspace(T, E, k, d, I) > (size_t)W4_NOALLOC_SCRATCH_BYTES) return W4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sa = scratch_address(&ws);
+  if (sa != W4_OK) return sa;
+  return w4a16_moe_layer(x, logits, T, E, k, d, I, w1_q, w1_s, w2_q, w2_s, activation, y, ws,
+                         (size_t)W4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

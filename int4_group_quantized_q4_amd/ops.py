@@ -260,6 +260,28 @@ def w4a16_moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation, y, ws, 
     check(st, "w4a16_moe_layer")
 
 
+def w4a16_moe_layer_noalloc(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation, y, stream=None):
+    """w4a16_moe_layer with the library's static device scratch in place of a
+    workspace (no allocation in the call; calls on one GPU must not overlap)."""
+    T, d = x.shape
+    E = logits.shape[1]
+    _dims(k, I)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError("logits must be [T=%d, E], got %s" % (T, tuple(logits.shape)))
+    dv = x.device
+    _need(logits, "logits", T * E * 4, dv)
+    _need(w1_q, "w1_q", E * 2 * I * d // 2, dv)
+    _need(w1_s, "w1_s", E * 2 * I * d // 32 * 2, dv)
+    _need(w2_q, "w2_q", E * d * I // 2, dv)
+    _need(w2_s, "w2_s", E * d * I // 32 * 2, dv)
+    _need(y, "y", T * d * 2, dv)
+    st = lib().w4a16_moe_layer_noalloc(
+        _ptr(x, "x", _BF16_LIKE), _ptr(logits, "logits", (torch.float32,)), T, E, k, d, I,
+        _ptr(w1_q, "w1_q", (torch.uint8,)), _ptr(w1_s, "w1_s", _BF16_LIKE), _ptr(w2_q, "w2_q", (torch.uint8,)),
+        _ptr(w2_s, "w2_s", _BF16_LIKE), activation, _ptr(y, "y", _BF16_LIKE), _stream(stream))
+    check(st, "w4a16_moe_layer_noalloc")
+
+
 # -------------------------------------------------------- allocating helpers
 def repack(w, stream=None):
     """bf16 [rows, K] -> (qweight uint8 [rows*K/2], scales bf16 [rows*K/32]

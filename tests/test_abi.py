@@ -202,3 +202,18 @@ def test_python_wrappers_reject_undersized_buffers():
                      ("ws", u8(need - 1))):
         with size_err:
             w4.w4a16_moe_layer(**dict(layer, **{key: bad}))
+
+
+def test_noalloc_layer_size_limit_on_host():
+    """The no-allocation layer refuses, before touching any device, a layer
+    whose workspace exceeds its static scratch; the limit is the header's."""
+    lib = _lib.lib()
+    assert w4.W4_NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert "#define W4_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+    assert lib.w4a16_moe_layer_workspace(290, 128, 8, 2816, 704) <= w4.W4_NOALLOC_SCRATCH_BYTES
+    assert lib.w4a16_moe_layer_workspace(300, 128, 8, 2816, 704) > w4.W4_NOALLOC_SCRATCH_BYTES
+    L = lib.w4a16_moe_layer_noalloc
+    assert L(FAKE, FAKE, 300, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_WORKSPACE
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 700, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_SHAPE
+    assert L(FAKE, FAKE, 64, 128, 17, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_ARG
