@@ -118,11 +118,18 @@ class MoeLayerSet:
         self.y = torch.empty(T, d, dtype=torch.bfloat16, device=device)
         gws = max(w4.w4a16_moe_gmm_workspace(T, R, E, d, 2 * I), w4.w4a16_moe_gmm_workspace(R, R, E, I, d))
         self.gws = torch.empty(max(16, gws), dtype=torch.uint8, device=device)
+        # decode batches take the streaming path of w4a16_moe_layer: top-k, the
+        # two matmuls over rows found from the ids (a and o at the routed rows),
+        # the combine with the identity row map
+        self.streaming = not w4.w4a16_moe_layer_sorted(T, E, k, d, I)
+        self.ident = torch.arange(R, dtype=torch.int32, device=device)
 
     def step(self, c, ev=None):
-        """One layer.  ev: None, 2 events (around the gate/up GEMM only) or 5
-        (between all four calls); each event record costs a few microseconds
-        of stream time."""
+        """One layer, as w4a16_moe_layer runs it.  ev: None, 2 events (around
+        the gate/up matmul only) or 5 (between the calls); each event record
+        costs a few microseconds of stream time."""
+        if self.streaming:
+            return self.step_streaming(c, ev)
         L = self.layers[c]
         T, d, I, E, k = self.T, self.d, self.I, self.E, self.k
         R = T * k
@@ -144,11 +151,33 @@ class MoeLayerSet:
         if full:
             ev[4].record()
 
+    def step_streaming(self, c, ev=None):
+        L = self.layers[c]
+        T, d, I, E, k = self.T, self.d, self.I, self.E, self.k
+        full = ev is not None and len(ev) == 5
+        if full:
+            ev[0].record()
+        w4.w4a16_moe_topk(L["logits"], k, self.ids, self.wts)
+        if ev is not None:
+            ev[1 if full else 0].record()
+        w4.w4a16_moe_gmm_ids(L["x"], self.ids, T, k, k, E, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
+                             self.act, w4.W4_OUT_BF16)
+        if ev is not None:
+            ev[2 if full else 1].record()
+        w4.w4a16_moe_gmm_ids(self.act, self.ids, T, k, 1, E, I, d, L["w2q"], L["w2s"], w4.W4_EPI_NONE, self.o,
+                             w4.W4_OUT_F32)
+        if full:
+            ev[3].record()
+        w4.w4a16_moe_combine(self.o, w4.W4_OUT_F32, self.ident, self.wts, T, k, d, self.y)
+        if full:
+            ev[4].record()
+
     def touched(self, c):
         """Experts with at least one routed row in copy c (host-side, untimed)."""
         self.step(c)
         torch.cuda.synchronize()
-        counts = torch.diff(self.offs).cpu().numpy()
+        ids = self.ids.cpu().numpy().ravel()
+        counts = np.bincount(ids, minlength=self.E)
         return int(np.count_nonzero(counts)), counts
 
 
@@ -244,7 +273,23 @@ def time_moe(cfg, steps, warmup, copies=3, seed=1234):
     torch.cuda.synchronize()
     parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evb])  # route, gmm1, gmm2, combine
     mean_touched = float(np.mean([touched[i % copies] for i in range(steps)]))
+    # the same layers through the one w4a16_moe_layer call (its own workspace)
+    lws = torch.empty(w4.w4a16_moe_layer_workspace(ls.T, ls.E, ls.k, ls.d, ls.I), dtype=torch.uint8, device=dev)
+    yl = torch.empty(ls.T, ls.d, dtype=torch.bfloat16, device=dev)
+
+    def layer_call(i):
+        L = ls.layers[i % copies]
+        w4.w4a16_moe_layer(L["x"], L["logits"], ls.k, ls.I, L["w1q"], L["w1s"], L["w2q"], L["w2s"],
+                           w4.W4_EPI_GEGLU_TANH, yl, lws)
+    warm_up(layer_call, 3)
+    la, lb = TimingEvent(), TimingEvent()
+    la.record()
+    for i in range(steps):
+        layer_call(i)
+    lb.record()
+    torch.cuda.synchronize()
     return {
+        "layer_call_ms": la.elapsed_time(lb) / steps,
         "ms_per_step": total_ms / steps,
         "gmm1_ms": float(g1.mean()),
         "gmm1_ms_p10_p90": [float(np.percentile(g1, 10)), float(np.percentile(g1, 90))],
@@ -272,7 +317,9 @@ def moe_decode_report(steps, warmup):
         "weight_bytes_per_layer": wbytes,
         "touched_experts": r["touched_experts"],
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
-        "kernel_ms_note": "gmm1 from the timed region; route, gmm2, combine from an instrumented pass after it",
+        "kernel_ms_note": "gmm1 from the timed region; route (top-k only: the matmuls find their rows in "
+                          "the ids), gmm2, combine from an instrumented pass after it",
+        "layer_ms_single_call": r["layer_call_ms"],
         "roofline": {
             "bound": "hbm",
             "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",

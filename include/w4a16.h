@@ -248,6 +248,34 @@ int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * w4a16_moe_topk -- the top-k part of w4a16_moe_route alone: topk_ids and
+ * topk_weights as defined there, with no sort.  Same limits; T == 0 enqueues
+ * nothing.
+ */
+int w4a16_moe_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                   hipStream_t stream);
+
+/*
+ * w4a16_moe_gmm_ids -- grouped W4A16 matmul whose rows come straight from the
+ * top-k ids, with no sorted plan ([RQ] "What changed in vLLM's TPU backend":
+ * the grouped matmul over the experts' packed int4 weights and 32-wide
+ * scales).  For every routed row r = t*k + j (expert e = topk_ids[r]):
+ *     acc[r][n] = sum_c x[r / row_div][c] * s_e[n][c/32] * q_e[n][c]     (fp32)
+ * and out[r][.] = epilogue(acc[r][.]) as in w4a16_moe_gmm.  Each workgroup
+ * finds its expert's rows by scanning the ids; rows are taken in increasing r.
+ *   x          in  [T*k / row_div][K] bf16 (row_div = k: one row per token;
+ *                  row_div = 1: one row per routed row)
+ *   topk_ids   in  [T][k] int32, each in [0, E), distinct within a token
+ *   qweight, scales  as in w4a16_moe_gmm
+ *   out        out [T*k][N] (W4_EPI_NONE) or [T*k][N/2] of out_dtype
+ * Requires T <= 256 (W4_ERR_SHAPE), k <= 16, E <= 256 and the w4a16_moe_gmm
+ * shape rules.  Uses the weight-streaming kernels (decode batches).
+ */
+int w4a16_moe_gmm_ids(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t k, int32_t row_div, int32_t E,
+                      int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales, int32_t epilogue,
+                      void* out, int32_t out_dtype, hipStream_t stream);
+
+/*
  * w4a16_moe_gmm -- grouped W4A16 matmul over expert row ranges.
  *
  * The grouped matmul with one scale per 32-wide group that dequantizes each
@@ -278,6 +306,13 @@ int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index,
 /*
  * w4a16_moe_combine -- y[t][n] = bf16( sum_{j<k} w[t][j] * o[row_to_sorted[t*k+j]][n] ),
  * summed in slot order j = 0..k-1 in fp32.
+ *
+ * The end of a mixture-of-experts layer: each token's output is its k active
+ * experts' outputs weighted by the router ([RQ] "The gap at 26B": 8 of 128
+ * experts run per token).  The weights are used as given (w4a16_moe_route
+ * passes the softmax probabilities at the chosen ids, not renormalised); the
+ * bf16 rounding happens once, on the sum, since the layer's activations are
+ * bf16 ([RQ] "What changed in vLLM's TPU backend").
  *   o              in  [T*k][N] of o_dtype (W4_OUT_F32 or W4_OUT_BF16)
  *   row_to_sorted  in  [T*k] int32; topk_weights in [T][k] fp32
  *   y              out [T][N] bf16
@@ -289,12 +324,18 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
 
 /*
  * w4a16_moe_layer -- one whole mixture-of-experts layer over W4A16 experts:
- * w4a16_moe_route, then w4a16_moe_gmm over the fused gate/up weights with the
- * gated epilogue (gather of the token rows fused into the operand loads), then
- * w4a16_moe_gmm over the down weights (fp32 rows), then w4a16_moe_combine.
- * Everything is enqueued on `stream` ([RQ] "What changed in vLLM's TPU
- * backend": the experts method loads the packed int4 weights and the 32-wide
- * scales itself and routes them to the grouped-matmul backend).
+ * top-k routing, the fused gate/up matmul with the gated epilogue, the down
+ * matmul (fp32 rows), and the weighted combine, all enqueued on `stream`.
+ * This is the experts method of [RQ] "What changed in vLLM's TPU backend":
+ * the packed int4 experts and their 32-wide group scales go straight to the
+ * grouped matmul.  Two paths, by w4a16_moe_layer_sorted():
+ *   streaming  (at most 64 rows per expert on average and T <= 256; the
+ *              default for decode batches) w4a16_moe_topk, w4a16_moe_gmm_ids
+ *              for the gate/up (row_div = k) and the down (row_div = 1)
+ *              matmuls, then w4a16_moe_combine (row r = t*k + j): no sort;
+ *   sorted     the full routing plan of w4a16_moe_route, then the two matmuls
+ *              gather their rows through it, then w4a16_moe_combine.
+ * Both store the intermediates a and o at the routed rows r = t*k + j.
  *   x       in  [T][d] bf16;  logits in [T][E] fp32
  *   w1_q    in  E * (2I)*d/2 bytes tile16 (rows [0, I) gate, [I, 2I) up);
  *   w1_s    in  E * 2I*d/32 bf16, tile16 scale layout
@@ -303,7 +344,7 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
  *   y       out [T][d] bf16
  *   ws      workspace of at least w4a16_moe_layer_workspace(T, E, k, d, I) bytes,
  *           16-byte aligned; it holds the routing plan (see w4a16_moe_layer_plan)
- *           and the intermediate activations
+ *           and the intermediate activations.  Its contents on entry do not matter.
  * Requires d % 32 == 0, I % 32 == 0 and the w4a16_moe_route limits.
  */
 size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I);
@@ -312,13 +353,22 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
                     int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * w4a16_moe_layer_sorted -- 1 when w4a16_moe_layer takes the sorted path for
+ * these sizes under the current kernel choice (w4a16_set_gemm_kernel), 0 when
+ * it takes the streaming path, W4_ERR_ARG for bad sizes.
+ */
+int w4a16_moe_layer_sorted(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I);
+
+/*
  * w4a16_moe_layer_plan -- byte offsets, inside a w4a16_moe_layer workspace, of
  * the routing plan and intermediates it leaves behind (for inspection):
  *   out[0] topk_ids [T][k] i32      out[1] topk_weights [T][k] f32
  *   out[2] expert_offsets [E+1] i32 out[3] sorted_rows [T*k] i32
  *   out[4] sorted_tokens [T*k] i32  out[5] row_to_sorted [T*k] i32
- *   out[6] route scratch            out[7] a: gated activations [T*k][I] bf16
- *   out[8] o: down-projection rows [T*k][d] f32 (sorted order)
+ *          (out[2..5]: sorted path only)
+ *   out[6] route scratch (sorted path)
+ *   out[7] a: gated activations [T*k][I] bf16, row r = t*k + j
+ *   out[8] o: down-projection rows [T*k][d] f32, row r = t*k + j
  * Returns W4_ERR_ARG for out == NULL or bad sizes.
  */
 int w4a16_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[9]);

@@ -177,6 +177,59 @@ int w4a16_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_
   return launch_status();
 }
 
+int w4a16_moe_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                   hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || k > 16) return W4_ERR_ARG;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (T == 0) return W4_OK;
+  if (!logits || !topk_ids || !topk_weights) return W4_ERR_ARG;
+  w4::launch_topk(logits, T, E, k, topk_ids, topk_weights, stream);
+  return launch_status();
+}
+
+// Shape and pointer checks shared by the two ids-mode matmuls.
+static int check_gmm_ids(const void* x, const int32_t* ids, int64_t T, int32_t k, int32_t E, int64_t K, int64_t N,
+                         const uint8_t* qweight, const uint16_t* scales, const void* out) {
+  if (T < 0 || k < 1 || k > 16 || E < 1 || E > 256 || k > E) return W4_ERR_ARG;
+  int st = check_matrix(N, K);
+  if (st != W4_OK) return st;
+  if (T > w4::kIdsMaxExpertRows || T * k > w4::kIdsMaxRows) return W4_ERR_SHAPE;
+  if (N * K / 2 >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (T == 0 || N == 0) return W4_OK;
+  if (K == 0) return W4_ERR_SHAPE;
+  if (!x || !ids || !qweight || !scales || !out) return W4_ERR_ARG;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(out)) return W4_ERR_ARG;
+  return W4_OK;
+}
+
+int w4a16_moe_gmm_ids(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t k, int32_t row_div, int32_t E,
+                      int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales, int32_t epilogue,
+                      void* out, int32_t out_dtype, hipStream_t stream) {
+  if (row_div != 1 && row_div != k) return W4_ERR_ARG;
+  if (epilogue != W4_EPI_NONE && epilogue != W4_EPI_GEGLU_TANH && epilogue != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  if (out_dtype != W4_OUT_BF16 && out_dtype != W4_OUT_F32) return W4_ERR_ARG;
+  if (epilogue != W4_EPI_NONE && out_dtype != W4_OUT_BF16) return W4_ERR_ARG;
+  int st = check_gmm_ids(x, topk_ids, T, k, E, K, N, qweight, scales, out);
+  if (st != W4_OK || T == 0 || N == 0) return st;
+  if (epilogue != W4_EPI_NONE && N % 32 != 0) return W4_ERR_SHAPE;
+  w4::GemmArgs a{};
+  a.x = x;
+  a.x_rows = T * k / row_div;
+  a.E = E;
+  a.R = T * k;
+  a.K = K;
+  a.N = N;
+  a.qweight = qweight;
+  a.scales = scales;
+  a.epilogue = epilogue;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.ids = topk_ids;
+  a.kslots = row_div;
+  w4::launch_gemm_skinny(a, stream);
+  return launch_status();
+}
+
 int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, const int32_t* expert_offsets,
                   int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales,
                   int32_t epilogue, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
@@ -257,6 +310,33 @@ size_t w4a16_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int
   return layer_gemm_ws_offset(p, T, k, d) + layer_gemm_ws_bytes(T, E, k, d, I);
 }
 
+// Which path a layer takes: the streaming kernels with rows found from the
+// top-k ids (few rows per expert, at most kIdsMaxExpertRows tokens), else the
+// sorted plan.
+static bool layer_sorted(const w4::GemmArgs& a1, const w4::GemmArgs& a2, int64_t T) {
+  const int policy = g_gemm_kernel.load(std::memory_order_relaxed);
+  const bool streaming = policy == W4_KERNEL_STREAM ||
+                         (policy == W4_KERNEL_AUTO && a1.R <= (int64_t)W4_TILED_MIN_ROWS * a1.E) ||
+                         !w4::gemm_tiled_supported(a1) || !w4::gemm_tiled_supported(a2);
+  return !(streaming && T <= w4::kIdsMaxExpertRows && a1.R <= w4::kIdsMaxRows);
+}
+
+int w4a16_moe_layer_sorted(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I) {
+  if (T < 0 || E < 1 || k < 1 || d < 0 || I < 0) return W4_ERR_ARG;
+  w4::GemmArgs a1{}, a2{};
+  a1.x_rows = T;
+  a1.E = a2.E = E;
+  a1.R = a2.R = T * k;
+  a2.x_rows = T * k;
+  a1.K = d;
+  a1.N = 2 * I;
+  a1.epilogue = W4_EPI_GEGLU_TANH;
+  a2.K = I;
+  a2.N = d;
+  a2.epilogue = W4_EPI_NONE;
+  return layer_sorted(a1, a2, T) ? 1 : 0;
+}
+
 // Host checks of a layer call, everything but the workspace: W4_OK to run,
 // kLayerEmpty when there is nothing to enqueue, else the error.
 static constexpr int kLayerEmpty = 1;
@@ -302,15 +382,64 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
   void* gws = base + layer_gemm_ws_offset(p, T, k, d);
   const size_t gws_bytes = layer_gemm_ws_bytes(T, E, k, d, I);
   const int64_t R = T * k;
+
+  // gate/up: h = x . W1^T with the gated activation -> a (routed-row order)
+  w4::GemmArgs a1{};
+  a1.x = x;
+  a1.x_rows = T;
+  a1.E = E;
+  a1.R = R;
+  a1.K = d;
+  a1.N = 2 * I;
+  a1.qweight = w1_q;
+  a1.scales = w1_s;
+  a1.epilogue = activation;
+  a1.out = act;
+  a1.out_dtype = W4_OUT_BF16;
+  // down: o = a . W2^T (fp32, routed-row order), then the weighted combine
+  w4::GemmArgs a2{};
+  a2.x = act;
+  a2.x_rows = R;
+  a2.E = E;
+  a2.R = R;
+  a2.K = I;
+  a2.N = d;
+  a2.qweight = w2_q;
+  a2.scales = w2_s;
+  a2.epilogue = W4_EPI_NONE;
+  a2.out = o;
+  a2.out_dtype = W4_OUT_F32;
+
+  if (!layer_sorted(a1, a2, T)) {
+    // Few rows per expert: no sort.  Each matmul workgroup finds its expert's
+    // rows in the top-k ids (w4a16_moe_topk, w4a16_moe_gmm_ids twice).
+    w4::launch_topk(logits, T, E, k, ids, wts, stream);
+    a1.ids = ids;
+    a1.kslots = k;
+    a2.ids = ids;
+    a2.kslots = 1;
+    w4::launch_gemm_skinny(a1, stream);
+    w4::launch_gemm_skinny(a2, stream);
+    w4::launch_combine(o, W4_OUT_F32, nullptr, wts, T, k, d, y, stream);
+    return launch_status();
+  }
+  // Many rows per expert: the routing plan sorts the rows by expert; the
+  // matmuls gather their rows through it and store a and o at the rows' own
+  // (routed) positions, where the combine reads them.
   st = w4a16_moe_route(logits, T, E, k, ids, wts, offs, srows, stoks, r2s, rws, p[7] - p[6], stream);
   if (st != W4_OK) return st;
-  st = w4a16_moe_gmm(x, T, stoks, offs, E, R, d, 2 * I, w1_q, w1_s, activation, act, W4_OUT_BF16, gws, gws_bytes,
-                     stream);
+  a1.row_index = stoks;
+  a1.offsets = offs;
+  a1.out_index = srows;
+  st = run_gemm(a1, gws, gws_bytes, stream);
   if (st != W4_OK) return st;
-  st = w4a16_moe_gmm(act, R, nullptr, offs, E, R, I, d, w2_q, w2_s, W4_EPI_NONE, o, W4_OUT_F32, gws, gws_bytes,
-                     stream);
+  a2.row_index = srows;
+  a2.offsets = offs;
+  a2.out_index = srows;
+  st = run_gemm(a2, gws, gws_bytes, stream);
   if (st != W4_OK) return st;
-  return w4a16_moe_combine(o, W4_OUT_F32, r2s, wts, T, k, d, y, stream);
+  w4::launch_combine(o, W4_OUT_F32, nullptr, wts, T, k, d, y, stream);
+  return launch_status();
 }
 
 // ---------------------------------------------------------------------------

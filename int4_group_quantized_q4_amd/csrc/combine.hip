@@ -1,6 +1,6 @@
 // Weighted combine of the experts' outputs back into token order:
 // y[t][n] = bf16( sum_{j<k} w[t][j] * o[row_to_sorted[t*k+j]][n] ), summed in
-// slot order in fp32.  One thread per (token, 8 consecutive columns); the rows
+// slot order in fp32 (o[t*k+j] when row_to_sorted is null).  One thread per (token, 8 consecutive columns); the rows
 // of 4 slots are loaded before any is summed, so their latencies overlap.
 
 #include "common.h"
@@ -21,7 +21,7 @@ __device__ __forceinline__ void combine_slots(const void* __restrict__ o, const 
   float wj[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) {
-    row[c] = row_to_sorted[t * k + j0 + c];
+    row[c] = row_to_sorted ? row_to_sorted[t * k + j0 + c] : t * k + j0 + c;
     wj[c] = w[t * k + j0 + c];
   }
   if constexpr (ODT == W4_OUT_F32) {

@@ -94,6 +94,76 @@ __device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn
 // fp32 -> bf16 bits, round to nearest even, by the hardware conversion.
 __device__ __forceinline__ uint16_t bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
+// Routed rows of expert e in a top-k id list ids[0 .. R) (routed row r = t*k + j
+// holds the j-th expert of token t): the r with ids[r] == e, in increasing
+// order, written to rows[0 .. min(count, cap)); returns count.  All NW waves of
+// the workgroup take part: in round q, wave w scans ids [512 (q NW + w), +512)
+// and a prefix over the waves' counts (s_cnt, NW ints of LDS) places its
+// rows, so each round costs one load latency (R <= 512: wave 0 alone).  Round 0's ids
+// are loaded by ids_batch() beforehand, so a caller can issue those loads
+// ahead of its other loads (vector loads complete in order: loads issued
+// before them would be waited for too).  Ends with a workgroup barrier.
+__device__ __forceinline__ void ids_batch(const int32_t* __restrict__ ids, int R, int batch, int v[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 512 * batch + 64 * q + lane;
+    v[q] = r < R ? ids[r] : -1;
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ int expert_rows_from_ids(const int32_t* __restrict__ ids, int R, int e, int* rows,
+                                                    int cap, int* s_cnt, int v[8]) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (R <= 512) {   // one batch: wave 0 alone, one barrier
+    if (wv == 0) {
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint64_t b = __ballot(v[q] == e);
+        const int pos = n + __popcll(b & below);
+        if (((b >> lane) & 1ull) && pos < cap) rows[pos] = 64 * q + lane;
+        n += __popcll(b);
+      }
+      if (lane == 0) s_cnt[0] = n;
+    }
+    __syncthreads();
+    return s_cnt[0];
+  }
+  int total = 0;
+  for (int round = 0; 512 * NW * round < R; ++round) {
+    if (round > 0) ids_batch(ids, R, NW * round + wv, v);
+    uint64_t b[8];
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      b[q] = __ballot(v[q] == e);
+      n += __popcll(b[q]);
+    }
+    if (lane == 0) s_cnt[wv] = n;
+    __syncthreads();
+    int base = total, all = total;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = s_cnt[w];
+      if (w < wv) base += c;
+      all += c;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int pos = base + __popcll(b[q] & below);
+      if (((b[q] >> lane) & 1ull) && pos < cap) rows[pos] = 512 * (NW * round + wv) + 64 * q + lane;
+      base += __popcll(b[q]);
+    }
+    total = all;
+    __syncthreads();   // rows written; s_cnt free for the next round
+  }
+  return total;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

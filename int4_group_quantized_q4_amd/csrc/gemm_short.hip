@@ -44,13 +44,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // NBF: full tile16 blocks per row (K / 128); the 0..3 groups past them form
 // the partial block.
-template <int NBF, int OUT>
+// IDS: rows from the top-k ids (GemmArgs::ids): activation row r / kslots,
+// output row r.
+template <int NBF, int OUT, bool IDS>
 __global__ void __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(3)))
 short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) {
   constexpr int CB = NBF > 0 ? NBF : 1;
   __shared__ __align__(16) uint8_t xs[16 * (2 * kMaxCols + 16)];
   __shared__ __align__(16) uint8_t ssc[kSW * 2 * 1024];
   __shared__ __align__(16) float ctab[(kMaxCols / kGroup) * 16];   // [G][16]: -136 x group sum of each row
+  __shared__ int s_rows[IDS ? kIdsMaxExpertRows : 1];              // the expert's routed rows
+  __shared__ int s_wcnt[kSW];                              // per-wave counts of the ids scan
 
   const int wg = short_xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
@@ -94,10 +98,18 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
   // without waiting for that read.
   u32x4 cwA[CB], cwB[CB], spA = {0u, 0u, 0u, 0u}, spB = {0u, 0u, 0u, 0u};
   uint32_t ctA[3] = {0u, 0u, 0u}, ctB[3] = {0u, 0u, 0u}, stA[3] = {0u, 0u, 0u}, stB[3] = {0u, 0u, 0u};
+  // (the ids go out before the tile: the scan must not wait for the tile to land)
+  int idv[8];
+  if constexpr (IDS) {
+    if (a.R > 512 || wv == 0) ids_batch(a.ids, (int)a.R, wv, idv);
+  }
   load_tile(cwA, ctA, spA, stA, 0);
 
   int64_t row_begin = 0, row_end = a.R;
-  if (a.offsets) {
+  if constexpr (IDS) {
+    row_end = __builtin_amdgcn_readfirstlane(
+        expert_rows_from_ids<kSW>(a.ids, (int)a.R, e, s_rows, kIdsMaxExpertRows, s_wcnt, idv));
+  } else if (a.offsets) {
     row_begin = a.offsets[e];
     row_end = a.offsets[e + 1];
   }
@@ -105,9 +117,20 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  // the output up to the expert's last row (R * N * ESZ < 2^31, checked on the host)
+  // sorted row i (of this expert's range) -> activation row and output row
+  auto xrow = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    if constexpr (IDS) return (int64_t)(s_rows[i] / a.kslots);
+    else return a.row_index ? (int64_t)a.row_index[i] : i;
+  };
+  auto orow = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    if constexpr (IDS) return (int64_t)s_rows[i];
+    else return a.out_index ? (int64_t)a.out_index[i] : i;
+  };
+  // the whole output (R * N * ESZ < 2^31, checked on the host); rows past the
+  // expert's count get the offset of the range's end, so their stores are dropped
   constexpr int ESZ = OUT == W4_OUT_F32 ? 4 : 2;
-  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(row_end * N * ESZ), kRsrcFlags);
+  const uint32_t orange = (uint32_t)(a.R * N * ESZ);
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, orange, kRsrcFlags);
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -125,7 +148,7 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
       for (int h = 0; h < 16 / kSW; ++h) {
         const int m = wv + kSW * h;
         if (m < cnt) {   // wave-uniform
-          const int64_t row = a.row_index ? (int64_t)a.row_index[row0 + m] : row0 + m;
+          const int64_t row = xrow(row0 + m);
           const uint16_t* src = a.x + row * K;
           for (int d = 0; d < nrow_dma; ++d) {
             int64_t col = (int64_t)d * 512 + 8 * lane;
@@ -160,7 +183,10 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
 
     const uint8_t* xa = xs + arow * XS + c * 16;
     const uint8_t* ca = reinterpret_cast<const uint8_t*>(ctab) + c * 16;   // rows 4c .. 4c+3
-    const uint32_t obase = (uint32_t)(((row0 + 4 * c) * N + r) * ESZ);
+    uint32_t obase[4];   // this lane's output rows 4c + q (past the count: dropped)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      obase[q] = 4 * c + q < cnt ? (uint32_t)((orow(row0 + 4 * c + q) * N + r) * ESZ) : orange;
     auto run_tile = [&](const u32x4* cw, const uint32_t* ct, const u32x4& sp, const uint32_t* st, int i,
                         int set) __attribute__((always_inline)) {
       const int t = tile_of(i);
@@ -198,11 +224,11 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
           const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(ct[j])), cb);
           acc += bf16_to_f32(st[j]) * p;
         }
-      // D rows = 4c + q, column = r; rows past the expert's last fall outside
-      // the output descriptor's range and are dropped
+      // D rows = 4c + q, column = r; rows past the expert's count have an
+      // offset at the end of the output descriptor's range and are dropped
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t off = obase + (uint32_t)((q * N + t * kTileRows) * ESZ);
+        const uint32_t off = obase[q] + (uint32_t)(t * kTileRows * ESZ);
         if constexpr (OUT == W4_OUT_F32)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[q]), ors, off, 0, 0);
         else
@@ -232,12 +258,20 @@ void launch_nbf(const GemmArgs& a, hipStream_t stream) {
   const int tiles = (int)(a.N / kTileRows);
   const int wg_per_expert = (tiles + kSW * kTPW - 1) / (kSW * kTPW);
   const int total = wg_per_expert * a.E;
-  if (a.out_dtype == W4_OUT_F32)
-    hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_F32>), dim3(total), dim3(64 * kSW), 0, stream, a, wg_per_expert,
-                       total, tiles);
-  else
-    hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_BF16>), dim3(total), dim3(64 * kSW), 0, stream, a, wg_per_expert,
-                       total, tiles);
+  if (a.ids) {
+    if (a.out_dtype == W4_OUT_F32)
+      hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_F32, true>), dim3(total), dim3(64 * kSW), 0, stream, a,
+                         wg_per_expert, total, tiles);
+    else
+      hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_BF16, true>), dim3(total), dim3(64 * kSW), 0, stream, a,
+                         wg_per_expert, total, tiles);
+  } else if (a.out_dtype == W4_OUT_F32) {
+    hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_F32, false>), dim3(total), dim3(64 * kSW), 0, stream, a,
+                       wg_per_expert, total, tiles);
+  } else {
+    hipLaunchKernelGGL((short_kernel<NBF, W4_OUT_BF16, false>), dim3(total), dim3(64 * kSW), 0, stream, a,
+                       wg_per_expert, total, tiles);
+  }
 }
 
 }  // namespace

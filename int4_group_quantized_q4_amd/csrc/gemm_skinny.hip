@@ -55,7 +55,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // D: code/scale blocks in flight per wave (ring depth); a chunk of staged
 // activations spans max(4, D) blocks so that ring slots are compile-time.
-template <int MAXT, int EPI, int OUT, int D>
+// IDS: rows from the top-k ids (GemmArgs::ids): activation row r / kslots,
+// output row r.
+template <int MAXT, int EPI, int OUT, int D, bool IDS>
 __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmArgs a, int wg_per_expert,
                                                                            int total_wg, int units_per_expert) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
@@ -71,16 +73,12 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   constexpr int SPL = SPB / 8;   // 16-byte loads per lane per span
   __shared__ __align__(16) uint8_t ssc[kWaves * SPBYTES];
 
+  __shared__ int s_rows[IDS ? kIdsMaxExpertRows : 1];   // the expert's routed rows
+  __shared__ int s_wcnt[kWaves];                              // per-wave counts of the ids scan
+
   const int wg = xcd_item(blockIdx.x, total_wg);
   const int e = wg / wg_per_expert;
   const int wgi = wg - e * wg_per_expert;
-  int64_t row_begin = 0, row_end = a.R;
-  if (a.offsets) {
-    row_begin = a.offsets[e];
-    row_end = a.offsets[e + 1];
-  }
-  if (row_begin >= row_end) return;   // the whole workgroup leaves together
-
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
@@ -112,6 +110,42 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   auto load_block = [&](int slot, int b) __attribute__((always_inline)) {
     cw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + 1024 * (int64_t)b + 16 * lane));
   };
+
+  int64_t row_begin = 0, row_end = a.R;
+  // The first pass's weight ring does not depend on the rows: it is issued
+  // before the row range is known (ids scan or offsets read) and that wait
+  // overlaps the weight stream's first latency.  Later passes load their ring
+  // in their own prologue, after the barrier that ends the previous pass.
+  // (The ids go out first: the scan must not wait for the ring to land.)
+  int idv[8];
+  if constexpr (IDS) {
+    if (a.R > 512 || wv == 0) ids_batch(a.ids, (int)a.R, wv, idv);
+  }
+  if (NBF > 0) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+  }
+  if constexpr (IDS) {
+    row_end = __builtin_amdgcn_readfirstlane(
+        expert_rows_from_ids<kWaves>(a.ids, (int)a.R, e, s_rows, kIdsMaxExpertRows, s_wcnt, idv));
+  } else if (a.offsets) {
+    row_begin = a.offsets[e];
+    row_end = a.offsets[e + 1];
+  }
+  if (row_begin >= row_end) {   // the whole workgroup leaves together
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  // sorted row i (of this expert's range) -> activation row and output row
+  auto xrow = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    if constexpr (IDS) return (int64_t)(s_rows[i] / a.kslots);
+    else return a.row_index ? (int64_t)a.row_index[i] : i;
+  };
+  auto orow = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    if constexpr (IDS) return (int64_t)s_rows[i];
+    else return a.out_index ? (int64_t)a.out_index[i] : i;
+  };
+
 
   // Scales of the full blocks travel in spans of SPB blocks (contiguous in the
   // tile's scale layout): 128-bit loads, one per lane per 8 blocks, parked in
@@ -182,8 +216,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       const int rr = __builtin_amdgcn_readfirstlane(p / PPR);
       const int pc = p - rr * PPR;
       const bool live = rr < cnt;
-      const int64_t srow = live ? (a.row_index ? (int64_t)a.row_index[row0 + rr] : row0 + rr)
-                                : (a.row_index ? (int64_t)a.row_index[row0] : row0);   // a valid row
+      const int64_t srow = xrow(live ? row0 + rr : row0);   // a valid row
       // (readfirstlane returns int: each half goes back through uint32_t so
       // the low half is not sign-extended into the high one)
       const uint64_t base = (uint64_t)(a.x + srow * K);
@@ -216,8 +249,10 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     if (NBF > 0) {
       u32x4 s0[SPL];
       span_load(s0, 0);
+      if (row0 != row_begin) {   // (the first pass's ring is already in flight)
 #pragma unroll
-      for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+        for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+      }
       span_store(s0);
     }
     stage_store(0);
@@ -331,7 +366,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
             const float g = (float)(__bf16)acc[tt][i];
             const float u = (float)(__bf16)up[i];
             const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
-            static_cast<uint16_t*>(a.out)[row * (N / 2) + (int64_t)unit * kTileRows + r] = bf16_rne(act * u);
+            static_cast<uint16_t*>(a.out)[orow(row) * (N / 2) + (int64_t)unit * kTileRows + r] = bf16_rne(act * u);
           }
         }
       }
@@ -345,8 +380,9 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
             const int64_t row = row0 + 16 * tt + 4 * c + i;
             if (row >= row_end) continue;
             const int64_t col = (int64_t)tile * kTileRows + r;
-            if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[row * N + col] = acc[tt][i];
-            else static_cast<uint16_t*>(a.out)[row * N + col] = bf16_rne(acc[tt][i]);
+            const int64_t orw = orow(row);
+            if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[orw * N + col] = acc[tt][i];
+            else static_cast<uint16_t*>(a.out)[orw * N + col] = bf16_rne(acc[tt][i]);
           }
         }
       }
@@ -354,8 +390,8 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   }
 }
 
-template <int MAXT, int D>
-void launch_m(const GemmArgs& a, hipStream_t stream) {
+template <int MAXT, int D, bool IDS>
+void launch_m_ids(const GemmArgs& a, hipStream_t stream) {
   const bool gated = a.epilogue != W4_EPI_NONE;
   const int units = (int)(gated ? a.N / 32 : a.N / 16);
   const int per_wg = gated ? kWaves / 2 : kWaves;
@@ -363,17 +399,23 @@ void launch_m(const GemmArgs& a, hipStream_t stream) {
   const int total = wg_per_expert * a.E;
   dim3 grid(total), block(64 * kWaves);
   if (a.epilogue == W4_EPI_GEGLU_TANH)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_GEGLU_TANH, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_GEGLU_TANH, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
                        wg_per_expert, total, units);
   else if (a.epilogue == W4_EPI_SWIGLU)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_SWIGLU, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_SWIGLU, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
                        wg_per_expert, total, units);
   else if (a.out_dtype == W4_OUT_F32)
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_F32, D>), grid, block, 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_F32, D, IDS>), grid, block, 0, stream, a,
                        wg_per_expert, total, units);
   else
-    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_BF16, D>), grid, block, 0, stream, a,
+    hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
                        wg_per_expert, total, units);
+}
+
+template <int MAXT, int D>
+void launch_m(const GemmArgs& a, hipStream_t stream) {
+  if (a.ids) launch_m_ids<MAXT, D, true>(a, stream);
+  else launch_m_ids<MAXT, D, false>(a, stream);
 }
 
 }  // namespace

@@ -509,8 +509,9 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
       const int64_t row = row_begin + rr;
       const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
       const int ex = a.xexp[src];
+      const int64_t dst = a.out_index ? (int64_t)a.out_index[row] : row;
       if constexpr (GATED) {
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + row * (N / 2) + r;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + dst * (N / 2) + r;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float g = (float)(__bf16)ldexpf(acc[i][t][q], ex);
@@ -519,11 +520,11 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
           orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)(act * u));
         }
       } else if constexpr (OUT == W4_OUT_F32) {
-        float* orow = static_cast<float*>(a.out) + row * N + r;
+        float* orow = static_cast<float*>(a.out) + dst * N + r;
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t) orow[tile[t] * kTileRows] = ldexpf(acc[i][t][q], ex);
       } else {
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + row * N + r;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + dst * N + r;
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t)
           orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[i][t][q], ex));

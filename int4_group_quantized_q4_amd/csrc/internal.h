@@ -31,7 +31,19 @@ struct GemmArgs {
   // set by launch_gemm_tiled: x as fp16 rows scaled by 2^-xexp[row]
   const uint16_t* xh;
   const int32_t* xexp;
+  // nullable: output row of sorted row i is out_index[i] (else i)
+  const int32_t* out_index;
+  // Rows from top-k ids (streaming kernels only; offsets, row_index and
+  // out_index are then null): expert e's rows are the routed rows r with
+  // ids[r] == e, in increasing r; the activation row of r is x[r / kslots]
+  // and its output row is r.  R = T * k routed rows, at most kIdsMaxRows.
+  const int32_t* ids;
+  int32_t kslots;
 };
+
+// Most routed rows of an ids-mode call (an expert holds at most T of them).
+constexpr int kIdsMaxRows = 4096;
+constexpr int kIdsMaxExpertRows = 256;
 
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 bool gemm_tiled_supported(const GemmArgs& a);
@@ -47,7 +59,10 @@ size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);
 void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
                   int32_t* offsets, int32_t* sorted_rows, int32_t* sorted_tokens, int32_t* row_to_sorted,
                   void* ws, hipStream_t stream);
+void launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                 hipStream_t stream);
 
+// row_to_sorted null: the rows of token t are o[t*k + j]
 void launch_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sorted, const float* w,
                     int64_t T, int32_t k, int64_t N, uint16_t* y, hipStream_t stream);
 

@@ -285,6 +285,15 @@ size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k) {
   return (size_t)(nchunks * E + R) * sizeof(int32_t);
 }
 
+void launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                 hipStream_t stream) {
+  if (T == 0) return;
+  const dim3 tg((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), tb(64 * kTopkWaves);
+  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+  else hipLaunchKernelGGL(topk_kernel<4>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+}
+
 void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
                   int32_t* offsets, int32_t* sorted_rows, int32_t* sorted_tokens, int32_t* row_to_sorted,
                   void* ws, hipStream_t stream) {
@@ -293,10 +302,7 @@ void launch_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t*
     return;
   }
   const int64_t R = T * k;
-  const dim3 tg((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), tb(64 * kTopkWaves);
-  if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
-  else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
-  else hipLaunchKernelGGL(topk_kernel<4>, tg, tb, 0, stream, logits, T, E, k, ids, weights);
+  launch_topk(logits, T, E, k, ids, weights, stream);
   if (R <= kSmallRows) {
     hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, ids, (int)R, E, k, offsets,
                        sorted_rows, sorted_tokens, row_to_sorted);

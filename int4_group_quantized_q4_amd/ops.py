@@ -175,6 +175,37 @@ def w4a16_moe_route(logits, k, topk_ids, topk_weights, expert_offsets, sorted_ro
     check(st, "w4a16_moe_route")
 
 
+def w4a16_moe_topk(logits, k, topk_ids, topk_weights, stream=None):
+    T, E = logits.shape
+    d = logits.device
+    _need(topk_ids, "topk_ids", T * k * 4, d)
+    _need(topk_weights, "topk_weights", T * k * 4, d)
+    st = lib().w4a16_moe_topk(_ptr(logits, "logits", (torch.float32,)), T, E, k,
+                              _ptr(topk_ids, "topk_ids", (torch.int32,)),
+                              _ptr(topk_weights, "topk_weights", (torch.float32,)), _stream(stream))
+    check(st, "w4a16_moe_topk")
+
+
+def w4a16_moe_gmm_ids(x, topk_ids, T, k, row_div, E, K, N, qweight, scales, epilogue, out, out_dtype, stream=None):
+    _dims(T, k, E, K, N)
+    if row_div not in (1, k):
+        raise ValueError("row_div must be 1 or k")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [rows, K=%d], got %s" % (K, tuple(x.shape)))
+    d = x.device
+    _need(x, "x", (T * k // row_div) * K * 2, d)
+    _need(topk_ids, "topk_ids", T * k * 4, d)
+    _need(qweight, "qweight", E * N * K // 2, d)
+    _need(scales, "scales", E * N * K // 32 * 2, d)
+    ncol = N // 2 if epilogue in (W4_EPI_GEGLU_TANH, W4_EPI_SWIGLU) else N
+    _need(out, "out", T * k * ncol * (4 if out_dtype == W4_OUT_F32 else 2), d)
+    st = lib().w4a16_moe_gmm_ids(
+        _ptr(x, "x", _BF16_LIKE), _ptr(topk_ids, "topk_ids", (torch.int32,)), T, k, row_div, E, K, N,
+        _ptr(qweight, "qweight", (torch.uint8,)), _ptr(scales, "scales", _BF16_LIKE), epilogue,
+        _ptr(out, "out", (torch.float32,) + _BF16_LIKE), out_dtype, _stream(stream))
+    check(st, "w4a16_moe_gmm_ids")
+
+
 def w4a16_moe_gmm_workspace(x_rows, R, E, K, N):
     return int(lib().w4a16_moe_gmm_workspace(x_rows, R, E, K, N))
 
@@ -230,6 +261,12 @@ def w4a16_moe_combine(o, o_dtype, row_to_sorted, topk_weights, T, k, N, y, strea
 
 def w4a16_moe_layer_workspace(T, E, k, d, I):
     return int(lib().w4a16_moe_layer_workspace(T, E, k, d, I))
+
+
+def w4a16_moe_layer_sorted(T, E, k, d, I):
+    """True when w4a16_moe_layer takes the sorted path for these sizes under
+    the current kernel choice (it then writes the sort outputs of the plan)."""
+    return bool(lib().w4a16_moe_layer_sorted(T, E, k, d, I))
 
 
 def w4a16_moe_layer_plan(T, E, k, d, I):
@@ -355,6 +392,7 @@ def moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation=W4_EPI_GEGLU_T
     w4a16_moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation, y, ws, stream)
     p = w4a16_moe_layer_plan(T, E, k, d, I)
     R = T * k
+    sorted_path = w4a16_moe_layer_sorted(T, E, k, d, I)
 
     def view(i, n, dt):
         nbytes = n * torch.empty((), dtype=dt).element_size()
@@ -369,5 +407,6 @@ def moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation=W4_EPI_GEGLU_T
         "row_to_sorted": view(5, R, torch.int32),
         "a": view(7, R * I, torch.bfloat16).view(R, I),
         "o": view(8, R * d, torch.float32).view(R, d),
+        "sorted": sorted_path,
     }
     return y, views

@@ -102,6 +102,20 @@ def test_tiled_kernel_needs_workspace():
         assert lib.w4a16_linear(FAKE, 300, 2816, FAKE, FAKE, 512, FAKE, None, 0, None) == w4.W4_ERR_WORKSPACE
 
 
+def test_streaming_calls_argument_errors():
+    lib = _lib.lib()
+    assert lib.w4a16_moe_topk(FAKE, 64, 128, 17, FAKE, FAKE, None) == w4.W4_ERR_ARG
+    assert lib.w4a16_moe_topk(None, 0, 128, 8, None, None, None) == w4.W4_OK
+    g = lib.w4a16_moe_gmm_ids
+    args = [FAKE, FAKE, 64, 8, 8, 128, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16, None]
+    bad = list(args); bad[4] = 3                    # row_div must be 1 or k
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[2] = 257                  # more tokens than the ids scan holds
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[12] = w4.W4_OUT_F32
+    assert g(*bad) == w4.W4_ERR_ARG
+
+
 def test_route_combine_layer_argument_errors():
     lib = _lib.lib()
     assert lib.w4a16_moe_route_workspace(64, 128, 8) > 0

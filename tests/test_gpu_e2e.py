@@ -105,8 +105,7 @@ def test_e2e_30_layer_repack_then_decode():
         if l in check_layers:
             torch.cuda.synchronize()
             saved[l] = dict(x=bits_host(x), y=bits_host(y), logits=logits[l].cpu().numpy(),
-                            ids=views["topk_ids"].cpu().numpy(), offsets=views["expert_offsets"].cpu().numpy(),
-                            perm=views["sorted_rows"].cpu().numpy())
+                            ids=views["topk_ids"].cpu().numpy(), weights=views["topk_weights"].cpu().numpy())
         x = (x.float() + y.float()).to(torch.bfloat16)   # residual stream, outside the library
     torch.cuda.synchronize()
     assert torch.isfinite(x.float()).all()
@@ -114,9 +113,10 @@ def test_e2e_30_layer_repack_then_decode():
     for l in check_layers:
         sv = saved[l]
         plan = oracle.route(sv["logits"], k)
+        # (256 tokens take the streaming path: each matmul finds its expert's
+        # rows in the ids, so the ids and weights are the whole plan)
         assert np.array_equal(sv["ids"], plan["ids"]), l
-        assert np.array_equal(sv["offsets"], plan["offsets"]), l
-        assert np.array_equal(sv["perm"], plan["perm"]), l
+        assert np.allclose(sv["weights"], plan["weights"], rtol=2e-6, atol=1e-9), l
         toks = np.sort(pick.choice(T, 4, replace=False))
         w1q, w1s, w2q, w2s = layers[l]
         ref = oracle.moe_layer(sv["x"][toks], sv["logits"][toks],

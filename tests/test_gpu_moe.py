@@ -249,27 +249,88 @@ def check_layer(cfg, label):
                             bf16_dev(w2t), w4.W4_EPI_GEGLU_TANH)
     torch.cuda.synchronize()
     ref = oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k, keep=True)
-    assert np.array_equal(views["expert_offsets"].cpu().numpy(), ref["plan"]["offsets"])
-    assert np.array_equal(views["sorted_tokens"].cpu().numpy(), ref["plan"]["tokens"])
+    plan = ref["plan"]
+    assert np.array_equal(views["topk_ids"].cpu().numpy(), plan["ids"])
+    assert np.allclose(views["topk_weights"].cpu().numpy(), plan["weights"], rtol=2e-6, atol=1e-9)
+    if views["sorted"]:   # the sort outputs exist on the sorted path only
+        assert np.array_equal(views["expert_offsets"].cpu().numpy(), plan["offsets"])
+        assert np.array_equal(views["sorted_tokens"].cpu().numpy(), plan["tokens"])
+    # a and o are stored at the routed rows r = t*k + j; the oracle's follow the sort
     a_ok, a_mx, a_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(views["a"])),
-                                                oracle.bf16_bits_to_f64(ref["a"]))
-    o_ok, o_mx, o_rms = oracle.within_tolerance(views["o"].cpu().numpy(), ref["o"])
+                                                oracle.bf16_bits_to_f64(ref["a"][plan["inv"]]))
+    o_ok, o_mx, o_rms = oracle.within_tolerance(views["o"].cpu().numpy(), ref["o"][plan["inv"]])
     y_ok, y_mx, y_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y)),
                                                 oracle.bf16_bits_to_f64(ref["y"]))
-    say("  a: %.2e/%.2e  o: %.2e/%.2e  y: %.2e/%.2e (max_rel/rms_rel)" % (a_mx, a_rms, o_mx, o_rms, y_mx, y_rms))
+    say("  %s path  a: %.2e/%.2e  o: %.2e/%.2e  y: %.2e/%.2e (max_rel/rms_rel)"
+        % ("sorted" if views["sorted"] else "streaming", a_mx, a_rms, o_mx, o_rms, y_mx, y_rms))
     assert a_ok and o_ok and y_ok
+    return views["sorted"]
 
 
 def test_moe_layer_decode_full_size():
-    check_layer(gen.MOE_DECODE, "moe-decode")
+    assert not check_layer(gen.MOE_DECODE, "moe-decode")
 
 
-def test_moe_layer_small_shapes():
-    cfg = dict(id=940, T=19, d=96, I=64, E=8, k=3, router="normal")
-    check_layer(cfg, "small")
+@pytest.mark.parametrize("kernel", [w4.W4_KERNEL_AUTO, w4.W4_KERNEL_TILED])
+def test_moe_layer_decode_both_paths(kernel):
+    """The 64-token layer on the streaming path (rows found from the ids, no
+    sort) and, forced, on the sorted tiled path."""
+    cfg = dict(gen.MOE_DECODE, id=942)
+    with w4.gemm_kernel(kernel):
+        assert check_layer(cfg, "moe-decode kernel=%d" % kernel) == (kernel == w4.W4_KERNEL_TILED)
+
+
+@pytest.mark.parametrize("cfg", [dict(id=940, T=19, d=96, I=64, E=8, k=3, router="normal"),
+                                 dict(id=943, T=1, d=2816, I=704, E=128, k=8, router="normal"),
+                                 dict(id=944, T=256, d=256, I=96, E=16, k=4, router="normal"),
+                                 dict(id=945, T=40, d=64, I=1056, E=8, k=2, router="normal"),
+                                 dict(id=946, T=300, d=128, I=64, E=64, k=1, router="normal")])
+def test_moe_layer_small_shapes(cfg):
+    """Streaming path with a 1-token batch, with many rows per expert
+    (multi-pass, 64 per expert), with K above the short kernel's limit (I =
+    1056: the down matmul on the long-K kernel), and more than 256 tokens (the
+    sorted path)."""
+    check_layer(cfg, "small T=%d" % cfg["T"])
 
 
 @pytest.mark.parametrize("kernel", [w4.W4_KERNEL_AUTO, w4.W4_KERNEL_STREAM])
 def test_moe_layer_prefill_full_size(kernel):
     with w4.gemm_kernel(kernel):
-        check_layer(gen.MOE_PREFILL, "moe-prefill kernel=%d" % kernel)
+        assert check_layer(gen.MOE_PREFILL, "moe-prefill kernel=%d" % kernel)   # over 256 tokens: sorted
+
+
+@pytest.mark.parametrize("T,d,I,E,k", [(64, 256, 96, 16, 4), (64, 2816, 704, 128, 8), (3, 64, 32, 8, 8),
+                                       (256, 128, 64, 16, 2)])
+def test_streaming_calls_topk_gmm_ids(T, d, I, E, k):
+    """The streaming path's calls on their own: top-k equals the routing plan's;
+    the gate/up and down matmuls over rows found from the ids match the
+    oracle's a and o (stored at the routed rows); the combine with the
+    identity row map gives the oracle's y."""
+    cfg = dict(id=947, T=T, d=d, I=I, E=E, k=k, router="normal")
+    x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s) = moe_inputs(cfg, T + d)
+    say("[streaming calls] T=%d d=%d I=%d E=%d k=%d" % (T, d, I, E, k))
+    dev = "cuda"
+    R = T * k
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    w4.w4a16_moe_topk(to_dev(logits), k, ids, wts)
+    a = torch.full((R, I), float("nan"), dtype=torch.bfloat16, device=dev)
+    o = torch.full((R, d), float("nan"), dtype=torch.float32, device=dev)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    w1q, w1s_d, w2q, w2s_d = to_dev(w1p), bf16_dev(w1t), to_dev(w2p), bf16_dev(w2t)
+    w4.w4a16_moe_gmm_ids(bf16_dev(x), ids, T, k, k, E, d, 2 * I, w1q, w1s_d, w4.W4_EPI_GEGLU_TANH, a, w4.W4_OUT_BF16)
+    w4.w4a16_moe_gmm_ids(a, ids, T, k, 1, E, I, d, w2q, w2s_d, w4.W4_EPI_NONE, o, w4.W4_OUT_F32)
+    ident = torch.arange(R, dtype=torch.int32, device=dev)
+    w4.w4a16_moe_combine(o, w4.W4_OUT_F32, ident, wts, T, k, d, y)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k, keep=True)
+    plan = ref["plan"]
+    assert np.array_equal(ids.cpu().numpy(), plan["ids"])
+    assert np.allclose(wts.cpu().numpy(), plan["weights"], rtol=2e-6, atol=1e-9)
+    a_ok, a_mx, a_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(a)),
+                                                oracle.bf16_bits_to_f64(ref["a"][plan["inv"]]))
+    o_ok, o_mx, o_rms = oracle.within_tolerance(o.cpu().numpy(), ref["o"][plan["inv"]])
+    y_ok, y_mx, y_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y)),
+                                                oracle.bf16_bits_to_f64(ref["y"]))
+    say("  a %.2e/%.2e  o %.2e/%.2e  y %.2e/%.2e" % (a_mx, a_rms, o_mx, o_rms, y_mx, y_rms))
+    assert a_ok and o_ok and y_ok
