@@ -66,6 +66,12 @@ TRAFFIC = {
 }
 
 
+def traffic_source(key):
+    rec = TRAFFIC[key]
+    return ("rocprofv3 FETCH_SIZE and WRITE_SIZE counter passes (profiles/gemm_hbm_traffic.md) taken on kernel "
+            "sources sha256 %s...; null once those sources change" % rec["sha256"][:12])
+
+
 def traffic_of(key):
     """Counter-measured HBM bytes (read + write) per launch, or None when the
     kernel's sources differ from those the counters were taken on."""
@@ -317,6 +323,7 @@ def moe_decode_report(steps, warmup):
         "weight_bytes_per_layer": wbytes,
         "touched_experts": r["touched_experts"],
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "gmm1_ms_p10_p90": r["gmm1_ms_p10_p90"],
         "kernel_ms_note": "gmm1 from the timed region; route (top-k only: the matmuls find their rows in "
                           "the ids), gmm2, combine from an instrumented pass after it",
         "layer_ms_single_call": r["layer_call_ms"],
@@ -328,12 +335,13 @@ def moe_decode_report(steps, warmup):
             "unit": "GB/s",
             "frac": w1bytes / (r["gmm1_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": traffic_of("decode_gmm1"),
+            "traffic_source": traffic_source("decode_gmm1"),
         },
     }
     return out, r["layerset"]
 
 
-def moe_prefill_report(steps, warmup):
+def moe_prefill_report(steps, warmup, keep=False):
     cfg = gen.MOE_PREFILL
     r = time_moe(cfg, steps, warmup)
     R = cfg["T"] * cfg["k"]
@@ -342,7 +350,7 @@ def moe_prefill_report(steps, warmup):
     flops2 = 2.0 * R * I * d
     gmm_ms = r["gmm1_ms"] + r["gmm2_ms"]
     tf = (flops1 + flops2) / (gmm_ms * 1e-3) / 1e12
-    return {
+    rep = {
         "workload": "moe-prefill: T=4096, d_model=2816, E=128, top-8 Zipf(1.1), expert hidden 704, int4 g32",
         "gmm_TFLOPs": tf,
         "gmm_frac_of_bf16_mfma": tf / BF16_MFMA_PEAK_TFLOPS,
@@ -350,17 +358,24 @@ def moe_prefill_report(steps, warmup):
         "ms_per_step": r["ms_per_step"],
         "useful_flops_per_layer": flops1 + flops2,
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
+        "gmm1_ms_p10_p90": r["gmm1_ms_p10_p90"],
         "kernel_ms_note": "gmm1 from the timed region; route, gmm2, combine from an instrumented pass after it",
+        "mfma_dtype": "fp16 MFMA on exact s*q weights and fp16 activation rows under a per-row power of two "
+                      "(exact bf16 products; fp16 and bf16 share the dense peak)",
         "roofline": {
             "bound": "mfma",
-            "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
+            "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue; fp16 MFMA on exact s*q)",
             "achieved": flops1 / (r["gmm1_ms"] * 1e-3) / 1e12,
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops1 / (r["gmm1_ms"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "traffic": traffic_of("prefill_gmm1"),
+            "traffic_source": traffic_source("prefill_gmm1"),
         },
     }
+    if keep:
+        return rep, r["layerset"]
+    return rep
 
 
 def cpu_baseline_decode(layerset):
@@ -403,6 +418,111 @@ def cpu_baseline_decode(layerset):
         "kind": "oracle",
         "sample": "one full moe-decode layer (64 tokens, %d touched experts), NumPy fp64, %.2f s" % (touched, dt),
     }
+
+
+# ----------------------------------------------------------------- ceilings
+def ceilings_report():
+    """Measured machine ceilings on this GPU (libw4probe.so): a read-only
+    stream of 2 GiB with 16-byte loads, and fp16 16x16x32 MFMAs with every
+    operand in registers.  The kernels' rates are quoted against these as well
+    as against the published peaks."""
+    import ctypes
+    path = os.path.join(ROOT, "int4_group_quantized_q4_amd", "libw4probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("%s is missing: run the build" % path)
+    lp = ctypes.CDLL(path)
+    lp.w4probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lp.w4probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    blocks = 256 * 16
+    out = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    run = lambda i: lp.w4probe_stream(buf.data_ptr(), nbytes, out.data_ptr(), blocks, st)
+    warm_up(run, 5)
+    a, b = TimingEvent(), TimingEvent()
+    a.record()
+    for i in range(10):
+        run(i)
+    b.record()
+    torch.cuda.synchronize()
+    stream_gbs = nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9
+    del buf
+    mblocks, iters = 256 * 4, 4096
+    mout = torch.empty(mblocks * 256, dtype=torch.float32, device=dev)
+    runm = lambda i: lp.w4probe_mfma(mout.data_ptr(), mblocks, iters, st)
+    warm_up(runm, 3)
+    a, b = TimingEvent(), TimingEvent()
+    a.record()
+    for i in range(5):
+        runm(i)
+    b.record()
+    torch.cuda.synchronize()
+    flops = 2.0 * 16 * 16 * 32 * 8 * iters * 4 * mblocks
+    mfma_tf = flops / (a.elapsed_time(b) / 5 * 1e-3) / 1e12
+    return {"hbm_read_stream_GBs": stream_gbs, "hbm_read_stream_frac_of_peak": stream_gbs / HBM_PEAK_GBS,
+            "mfma_f16_TFLOPs": mfma_tf, "mfma_f16_frac_of_peak": mfma_tf / BF16_MFMA_PEAK_TFLOPS,
+            "note": "read-only stream of 2 GiB (16-byte loads) and register-only fp16 16x16x32 MFMA loops, "
+                    "measured in this run"}
+
+
+def cpu_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def cpu_baseline_extra(prefill_set=None):
+    """The oracle on bounded samples of the repack and prefill workloads."""
+    import oracle
+    out = {}
+    rng = gen.rng_for(5, 900)
+    n_groups = 1 << 19
+    src = gen.ongrid_source(rng, n_groups // 88 // 16 * 16 or 16, 2816, *gen.MOE_E2E["peak"])
+    groups = src["w_bits"].size // 32
+    t0 = time.perf_counter()
+    oracle.repack_groups(src["w_bits"].reshape(-1, 32))
+    dt = time.perf_counter() - t0
+    out["repack"] = {"value": groups / dt, "unit": "groups/s", "cores": cpu_threads(), "kind": "oracle",
+                     "sample": "%d on-grid groups (rows of 2816, peak level 4..8), %.2f s" % (groups, dt)}
+    if prefill_set is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import layout
+        ls = prefill_set
+        L = ls.layers[0]
+        E, I, d, k = ls.E, ls.I, ls.d, ls.k
+        toks = 24
+        x = L["x"][:toks].view(torch.int16).cpu().numpy().view(np.uint16)
+        logits = L["logits"][:toks].cpu().numpy()
+        used = np.unique(oracle.route(logits, k)["ids"])
+
+        def codes_of(packed, rows, K):
+            byte, shift = layout._index(rows, K)
+            per = packed.cpu().numpy().reshape(E, rows * K // 2)
+            v = np.zeros((E, rows, K), dtype=np.int8)
+            for e in used:
+                v[e] = ((per[e][byte] >> shift) & 0xF).astype(np.int16) - 8
+            return v
+
+        def scales_of(tiled, rows, K):
+            t = tiled.cpu().numpy().view(np.uint16).reshape(E, -1)
+            s = np.zeros((E, rows, K // 32), dtype=np.uint16)
+            for e in used:
+                s[e] = layout.decode_scales(t[e], rows, K)
+            return s
+
+        w1c, w2c = codes_of(L["w1q"], 2 * I, d), codes_of(L["w2q"], d, I)
+        w1s, w2s = scales_of(L["w1s"], 2 * I, d), scales_of(L["w2s"], d, I)
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, logits, w1c, w1s, w2c, w2s, k=k)
+        dt = time.perf_counter() - t0
+        flops = 2.0 * toks * k * (d * 2 * I + I * d)
+        out["moe_prefill"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+                              "sample": "%d of the 4096 Zipf-routed prefill tokens (%d experts), NumPy fp64, %.2f s"
+                                        % (toks, len(used), dt)}
+    return out
 
 
 # ------------------------------------------------------------- dense decode
@@ -602,6 +722,7 @@ def main():
                              "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip dense decode, e2e and the ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -624,13 +745,23 @@ def main():
                                             "int4 group 32 + bf16 scales", "weight_sets_rotated": 3},
                      "roofline": rep.pop("roofline")})
         line["decode"] = rep
+        pset = None
         if not args.no_prefill:
             log("moe-prefill")
-            pre = moe_prefill_report(max(10, args.steps // 5), max(2, args.warmup // 2))
+            pre, pset = moe_prefill_report(max(10, args.steps // 5), max(2, args.warmup // 2), keep=True)
             line["prefill"] = pre
+        if not args.no_extras:
+            log("dense decode")
+            line["dense_decode"] = {"workload": "w4a16_linear K=4096 N=14336, 33,030,144 weight bytes per call",
+                                    **dense_decode_report(max(20, args.steps // 2), args.warmup)}
+            log("e2e (30-layer repack, then 256-token decode)")
+            line["e2e"] = e2e_report(3, 2)
+            log("ceilings")
+            line["ceilings"] = ceilings_report()
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle)")
             line["cpu_baseline"] = cpu_baseline_decode(ls)
+            line["cpu_baseline_extra"] = cpu_baseline_extra(pset)
     elif args.workload == "moe-prefill":
         pre = moe_prefill_report(args.steps, args.warmup)
         line.update({"value": pre["gmm_TFLOPs"], "unit": "TFLOP/s", "ms_per_step": pre["ms_per_step"],

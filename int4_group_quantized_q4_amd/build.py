@@ -3,8 +3,9 @@
     python -m int4_group_quantized_q4_amd.build
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel)
-and the objects are linked into int4_group_quantized_q4_amd/libw4a16.so.  The
-library is always rebuilt when this runs.
+and the objects are linked into int4_group_quantized_q4_amd/libw4a16.so; the
+bench's ceiling kernels (probe/ceilings.hip) go to libw4probe.so.  Both are
+always rebuilt when this runs.
 """
 
 import concurrent.futures
@@ -38,8 +39,28 @@ COMMON_FLAGS = [
 ]
 
 
+PROBE = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libw4probe.so")
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build_probe(verbose=True):
+    """libw4probe.so: the bench's machine-ceiling kernels (not part of the ABI)."""
+    src = os.path.join(PROBE, "ceilings.hip")
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    # accumulators in VGPRs: in the accumulator-register form the compiler
+    # rotates the eight chains through copies on every iteration
+    cmd = [HIPCC] + COMMON_FLAGS + ["-mllvm", "-amdgpu-mfma-vgpr-form", "-shared", src, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("[build] wrote %s" % PROBE_LIB)
+    return PROBE_LIB
 
 
 def _compile(src):
@@ -73,6 +94,7 @@ def build(verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print("[build] wrote %s" % LIB)
+    build_probe(verbose)
     return LIB
 
 
