@@ -33,6 +33,11 @@
 //    gives 1024 + u, minus 1032 gives q, times the fp16 scale gives s*q.
 // Gated epilogue: a wave's 4 column tiles are 2 gate tiles and the matching 2
 // up tiles, so act(gate) * up is formed in registers.
+// Padding: an item holding at most 64 rows (an expert's last row tile) runs a
+// copy of the pipeline with MFMAs for 4 row tiles instead of 8, and in a
+// matrix's last column block the waves left without weight tiles skip the
+// expansion and the MFMAs (they still stage activations and meet the
+// barriers).
 // Scheduling: block b takes item (expert, row tile, column block) with the
 // column block fastest, dealt so that consecutive items share an XCD and its
 // L2: the row tile's activations and the expert's weights are re-read from L2.
@@ -362,9 +367,10 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   };
 
   // fast path: group g (0..3) of the block in slot SLOT, B = s*q exactly in fp16
-  auto fast_group = [&](const uint8_t* Ab, int apos, auto SLOT, auto GRP) __attribute__((always_inline)) {
+  auto fast_group = [&](const uint8_t* Ab, int apos, auto SLOT, auto GRP, auto ROWT) __attribute__((always_inline)) {
     constexpr int sl = decltype(SLOT)::value;
     constexpr int g = decltype(GRP)::value;
+    constexpr int mtv = decltype(ROWT)::value;
     h8 B[WN_TILES];
 #pragma unroll
     for (int t = 0; t < WN_TILES; ++t) {
@@ -379,10 +385,11 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         B[t][2 * d + 1] = q2[1];
       }
     }
-    // every row tile, also those past the expert's count (never stored):
-    // straight-line code lets the operand reads run ahead of the MFMAs
+    // every row tile of the variant, also those past the expert's count
+    // (never stored): straight-line code lets the operand reads run ahead of
+    // the MFMAs
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < mtv; ++i) {
       const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
 #pragma unroll
       for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A, B[t], acc[i][t]);
@@ -402,7 +409,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // The barrier then makes every wave's DMA visible and frees buffer s % NST,
   // which the next stage's DMA refills.
   const int last_st = S - 1;
-  auto stage = [&](int s, auto SLOT, auto HALF, auto RING) __attribute__((always_inline)) {
+  auto stage = [&](int s, auto SLOT, auto HALF, auto RING, auto ROWT) __attribute__((always_inline)) {
     constexpr int sl = decltype(SLOT)::value;
     constexpr int h = decltype(HALF)::value;
     constexpr int j = decltype(RING)::value;   // s % NST
@@ -414,9 +421,12 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     // waited for at once
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* Ab = slot_buf(RING);
-    if constexpr (h == 0) block_scales(s >> 1, SLOT);
-    fast_group(Ab, apos0, SLOT, std::integral_constant<int, 2 * h>{});
-    if (2 * s + 1 < G) fast_group(Ab, apos1, SLOT, std::integral_constant<int, 2 * h + 1>{});
+    // a wave without weight tiles (last column block) only stages and waits
+    if (active) {
+      if constexpr (h == 0) block_scales(s >> 1, SLOT);
+      fast_group(Ab, apos0, SLOT, std::integral_constant<int, 2 * h>{}, ROWT);
+      if (2 * s + 1 < G) fast_group(Ab, apos1, SLOT, std::integral_constant<int, 2 * h + 1>{}, ROWT);
+    }
     if constexpr (h == 0) wait_vm<(NST - 2) * AQ + 2 * WN_TILES>();
     else wait_vm<2 * AQ>();
     barrier_only();
@@ -431,17 +441,23 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     wait_vm<(NST - 2) * AQ>();
     barrier_only();
 
-    int s = 0;
+    // the stages with MFMAs for all MT row tiles, or (an item of at most 64
+    // rows: the tail of an expert) for the first MT/2
+    auto pipeline = [&](auto ROWT) __attribute__((always_inline)) {
+      int s = 0;
 #pragma unroll 1
-    for (; s + 3 < S; s += 4) {
-      stage(s, I<0>{}, I<0>{}, I<0>{});
-      stage(s + 1, I<0>{}, I<1>{}, I<1>{});
-      stage(s + 2, I<1>{}, I<0>{}, I<2>{});
-      stage(s + 3, I<1>{}, I<1>{}, I<3>{});
-    }
-    if (s < S) stage(s, I<0>{}, I<0>{}, I<0>{});
-    if (s + 1 < S) stage(s + 1, I<0>{}, I<1>{}, I<1>{});
-    if (s + 2 < S) stage(s + 2, I<1>{}, I<0>{}, I<2>{});
+      for (; s + 3 < S; s += 4) {
+        stage(s, I<0>{}, I<0>{}, I<0>{}, ROWT);
+        stage(s + 1, I<0>{}, I<1>{}, I<1>{}, ROWT);
+        stage(s + 2, I<1>{}, I<0>{}, I<2>{}, ROWT);
+        stage(s + 3, I<1>{}, I<1>{}, I<3>{}, ROWT);
+      }
+      if (s < S) stage(s, I<0>{}, I<0>{}, I<0>{}, ROWT);
+      if (s + 1 < S) stage(s + 1, I<0>{}, I<1>{}, I<1>{}, ROWT);
+      if (s + 2 < S) stage(s + 2, I<1>{}, I<0>{}, I<2>{}, ROWT);
+    };
+    if (nmt > MT / 2) pipeline(I<MT>{});
+    else pipeline(I<MT / 2>{});
     // the loads issued past the end are still in flight: drain before the
     // block's LDS is released
     wait_vm<0>();
