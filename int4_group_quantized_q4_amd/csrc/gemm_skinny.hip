@@ -18,10 +18,12 @@
 // scales).
 //
 // Per 4-group block: the nibbles become bf16 136+q with one shift and one
-// and-or per pair (biased_pairs); a first MFMA against a constant -136 operand
-// gives -136*sum(x) per row and group and is the accumulator input of the MFMA
-// against the biased codes, so each group's partial sum sum(x*q) comes out of
-// the matrix core; the VALU adds scale * partial into the fp32 accumulator.
+// and-or per pair (biased_pairs).  When a chunk of activations is staged, each
+// row's sum over each group is formed from the staged registers and -136 x
+// that sum goes to a small LDS table beside the chunk; the table entry is the
+// accumulator input of the MFMA against the biased codes, so each group's
+// partial sum sum(x*q) comes out of the matrix core in one MFMA; the VALU adds
+// scale * partial into the fp32 accumulator.
 // Rows beyond the expert's count read a valid row; their results are never
 // stored.
 
@@ -73,6 +75,9 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   constexpr int SPL = SPB / 8;   // 16-byte loads per lane per span
   __shared__ __align__(16) uint8_t ssc[kWaves * SPBYTES];
 
+  // -136 x each staged row's group sums, per staging buffer: [buffer][group of the chunk][row]
+  constexpr int TROWS = 16 * MAXT;
+  __shared__ __align__(16) float ctab[2 * CB * 4 * TROWS];
   __shared__ int s_rows[IDS ? kIdsMaxExpertRows : 1];   // the expert's routed rows
   __shared__ int s_wcnt[kWaves];                              // per-wave counts of the ids scan
 
@@ -184,7 +189,6 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       }
   }
 
-  const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // Activation staging: chunk ch (columns [ch*KC, ch*KC+KC)) of the pass's rows
@@ -227,6 +231,16 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       xdst[q] = rr * XS + pc * 16;
       xoff[q] = (uint32_t)(pc * 16);
     }
+    // a piece's group inside the chunk and its first lane: a group is 4
+    // consecutive pieces of a row, held by 4 consecutive lanes
+    int tidx[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int p = (int)threadIdx.x + q * 64 * kWaves;
+      const int rr = p / PPR;
+      const int pc = p - rr * PPR;
+      tidx[q] = (pc & 3) == 0 ? (pc >> 2) * TROWS + rr : -1;
+    }
     u32x4 xr[NP];
     auto stage_load = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
@@ -238,8 +252,18 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     };
     auto stage_store = [&](int ch) __attribute__((always_inline)) {
       uint8_t* buf = xs + (ch & 1) * XBUF;
+      float* tb = ctab + (ch & 1) * (CB * 4 * TROWS);
 #pragma unroll
-      for (int q = 0; q < NP; ++q) *reinterpret_cast<u32x4*>(buf + xdst[q]) = xr[q];
+      for (int q = 0; q < NP; ++q) {
+        *reinterpret_cast<u32x4*>(buf + xdst[q]) = xr[q];
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sum += bf16_to_f32(xr[q][k] & 0xFFFFu) + bf16_to_f32(xr[q][k] >> 16);
+        // quad sums: lanes 4i .. 4i+3 hold the group's four pieces
+        sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+        sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+        if (tidx[q] >= 0) tb[tidx[q]] = -136.f * sum;
+      }
     };
 
     // every load of the pass's start is issued before the first wait: the
@@ -268,7 +292,8 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
 
     // one block: MFMAs on the slot's codes, then refill the slot with block bn
     // (after the slot's last use, so no register copies are needed)
-    auto do_block = [&](const uint8_t* xb, int b, int lb, int slot, int bn) __attribute__((always_inline)) {
+    auto do_block = [&](const uint8_t* xb, const float* tb, int b, int lb, int slot, int bn)
+                        __attribute__((always_inline)) {
       const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + (b % SPB) * 128 + 8 * r);
       const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16),
                            bf16_to_f32(sv[1] & 0xFFFFu), bf16_to_f32(sv[1] >> 16)};
@@ -279,11 +304,16 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
         for (int tt = 0; tt < MAXT; ++tt)
           if (tt < ntt) {
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(xb + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
-            const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+            const f32x4 cb = *reinterpret_cast<const f32x4*>(tb + (lb * 4 + j) * TROWS + 16 * tt + 4 * c);
             const f32x4 p = mfma16x16x32(A, B, cb);
             acc[tt] += sc[j] * p;
           }
       }
+      // the block's accumulation happens here: left free, the code generator
+      // defers these adds past the scheduling barrier below and every
+      // block's MFMA results stay live until the end of the chunk
+#pragma unroll
+      for (int tt = 0; tt < MAXT; ++tt) asm volatile("" : "+v"(acc[tt]));
       load_block(slot, bn);
       __builtin_amdgcn_sched_barrier(0);   // issue the refill here, not later
     };
@@ -298,10 +328,11 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       const int chn = ch + 1 < nch ? ch + 1 : nch - 1;
       stage_load(chn);
       const uint8_t* xb = xs + (ch & 1) * XBUF;
+      const float* tb = ctab + (ch & 1) * (CB * 4 * TROWS);
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb) {
         const int bn = ch * CB + lb + D;
-        do_block(xb, ch * CB + lb, lb, lb % D, bn < NBF ? bn : NBF - 1);
+        do_block(xb, tb, ch * CB + lb, lb, lb % D, bn < NBF ? bn : NBF - 1);
       }
       stage_store(chn);
       __syncthreads();
@@ -323,9 +354,10 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     if (nfull < nch) {
       const int ch = nfull;
       const uint8_t* xb = xs + (ch & 1) * XBUF;
+      const float* tb = ctab + (ch & 1) * (CB * 4 * TROWS);
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb)
-        if (ch * CB + lb < NBF) do_block(xb, ch * CB + lb, lb, lb % D, NBF - 1);
+        if (ch * CB + lb < NBF) do_block(xb, tb, ch * CB + lb, lb, lb % D, NBF - 1);
       if (gtail > 0) {
         const int lb = NBF - ch * CB;   // local index of the partial block
 #pragma unroll
@@ -336,7 +368,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
             for (int tt = 0; tt < MAXT; ++tt)
               if (tt < ntt) {
                 const bf16x8 A = *reinterpret_cast<const bf16x8*>(xb + arow[tt] * XS + (lb * 4 + j) * 64 + c * 16);
-                const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+                const f32x4 cb = *reinterpret_cast<const f32x4*>(tb + (lb * 4 + j) * TROWS + 16 * tt + 4 * c);
                 const f32x4 p = mfma16x16x32(A, B, cb);
                 acc[tt] += st[j] * p;
               }
