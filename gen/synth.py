@@ -130,6 +130,23 @@ def router_logits(rng, T, E, law="normal", zipf_s=1.1):
 
 
 # ---------------------------------------------------------------- device draws
+# FP8 comparison experts: E4M3 codes and one fp32 scale per output channel
+FP8_SCALE_LO, FP8_SCALE_HI = 5e-4, 2e-3
+
+
+def fp8_codes(rng, shape):
+    """E4M3 codes drawn uniformly from the 254 finite patterns: draws 0..126
+    are codes 0x00..0x7E, draws 127..253 codes 0x80..0xFE (the NaN patterns
+    0x7F and 0xFF are never drawn)."""
+    u = rng.integers(0, 254, size=shape)
+    return (u + (u >= 127)).astype(np.uint8)
+
+
+def fp8_scales(rng, shape):
+    """fp32 per-channel scales, log-uniform in [FP8_SCALE_LO, FP8_SCALE_HI]."""
+    return _loguniform_f32(rng, shape, FP8_SCALE_LO, FP8_SCALE_HI)
+
+
 def torch_generator(device, seed):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -184,3 +201,15 @@ def ongrid_source_t(gen, rows, K, peak_lo, peak_hi, device, export=False):
         s0 = (s0.view(torch.int32) & int(np.int32(np.uint32(0xFFF80000).view(np.int32)))).view(torch.float32)
     w = (s0[..., None] * q.to(torch.float32)).to(torch.bfloat16).reshape(rows, K)
     return w, q.to(torch.int8).reshape(rows, K), s0.to(torch.bfloat16).view(torch.int16)
+
+
+def fp8_codes_t(gen, shape, device):
+    """Device version of ``fp8_codes``."""
+    u = torch.randint(0, 254, shape, dtype=torch.int32, device=device, generator=gen)
+    return (u + (u >= 127).to(torch.int32)).to(torch.uint8)
+
+
+def fp8_scales_t(gen, shape, device):
+    """Device version of ``fp8_scales``."""
+    u = torch.rand(shape, dtype=torch.float32, device=device, generator=gen)
+    return torch.exp(np.log(FP8_SCALE_LO) + u * (np.log(FP8_SCALE_HI) - np.log(FP8_SCALE_LO)))

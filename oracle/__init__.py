@@ -40,6 +40,18 @@ Parity status of each function (which pins it, see tests/test_oracle_*.py):
                                   pinned (hand-computed exact vectors that
                                   separate the normwise figures from element-wise
                                   or max|y|-based ones; zero and scaled references)
+  fp8.e4m3_decode / e4m3_encode   pinned (torch float8_e4m3fn on every code and
+                                  on random values; brute-force nearest value;
+                                  midpoints to the even code; saturation)
+  fp8.quantize_rows               pinned (amax lands on +-448; zero rows; codes
+                                  equal torch's conversion of the fp32 quotients)
+  fp8.linear                      pinned (exact integer matmul; row/column scales)
+  fp8.moe_layer                   pinned (E=1, k=1 equals the dense FP8 MLP
+                                  composed from torch fp8 conversion and float64
+                                  ops)
+
+The FP8 (W8A8) leg in fp8.py is the comparison path the pages set against
+W4A16 ([RQ] "What happened"; [VG] "2. What you can quantize").
 """
 
 from .bf16 import (
