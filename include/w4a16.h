@@ -395,6 +395,69 @@ int w4a16_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, i
                             int64_t I, const uint8_t* w1_q, const uint16_t* w1_s, const uint8_t* w2_q,
                             const uint16_t* w2_s, int32_t activation, uint16_t* y, hipStream_t stream);
 
+/* ---------------------------------------------------------------- FP8 (W8A8)
+ * The comparison path: the same MoE layer over FP8 experts, run natively on the
+ * FP8 matrix cores.  [RQ] "Repacked QAT Gemma 4 26B-A4B serves on one TPU v6e at
+ * 1.9x FP8 throughput", section "What happened" (the W4A16 build against an FP8
+ * build of the same model); [VG] "Compression Without Regret", sections "2. What
+ * you can quantize" and "3. The precision ladder" (FP8 quantizes weights and
+ * activations and multiplies natively in low precision).  The pages fix neither
+ * the encoding nor the scales; this library takes OCP E4M3 codes (largest finite
+ * magnitude 448, no infinities, 0x7F/0xFF NaN), one fp32 scale per weight row
+ * (output channel) and activations quantized per row at run time.
+ */
+
+/*
+ * w8a8_quantize_rows -- per-row dynamic E4M3 quantization.
+ *   x      in  [rows][K] bf16 (finite)
+ *   q      out [rows][K] E4M3 codes
+ *   scale  out [rows] fp32: amax / 448 (one IEEE fp32 division; 1.0 for a row of
+ *          zeros); q = E4M3(clamp(x / scale, -448, 448)), x / scale one IEEE fp32
+ *          division, rounded to nearest even.
+ * K % 32 == 0.  x and q 16-byte aligned, scale 4-byte aligned.
+ */
+int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale, hipStream_t stream);
+
+/*
+ * w8a8_moe_gmm -- grouped FP8 matmul over expert row ranges (the layout of
+ * w4a16_moe_gmm with byte codes and fp32 row scales):
+ *   out[i][n] = epilogue(x_scale[src(i)] * w_scale[e][n] *
+ *                        sum_k E4M3(xq[src(i)][k]) * E4M3(wq[e][n][k]))
+ * for sorted row i of expert e (offsets[e] <= i < offsets[e+1]), src(i) =
+ * row_index[i] (or i when row_index is NULL), fp32 accumulation.
+ *   xq, x_scale      in  [x_rows][K] E4M3 codes, [x_rows] fp32
+ *   row_index        in  [R] or NULL
+ *   expert_offsets   in  [E+1], or NULL with E == 1 (rows [0, R) are expert 0's)
+ *   wq, w_scale      in  [E][N][K] E4M3 codes (row-major), [E][N] fp32
+ *   epilogue         W4_EPI_* (gated: first N/2 rows gate, last N/2 up;
+ *                    out is [R][N/2] bf16)
+ *   out              out [R][N] (W4_EPI_NONE) of out_dtype, at the sorted rows
+ * K % 32 == 0; N % 16 == 0 with N/16 a multiple of 4 (plain) or N/32 even
+ * (gated); E <= 256; x_rows*K, N*K < 2^31.  Few rows per expert (at most 32 on
+ * average) take the weight-streaming kernel, more the 128-row tiled one.
+ */
+int w8a8_moe_gmm(const uint8_t* xq, const float* x_scale, int64_t x_rows, const int32_t* row_index,
+                 const int32_t* expert_offsets, int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* wq,
+                 const float* w_scale, int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream);
+
+/*
+ * w8a8_moe_layer -- the MoE layer over FP8 experts, one call: route (as
+ * w4a16_moe_route), quantize x per token, the gate/up grouped matmul with the
+ * gated activation (a, bf16, sorted rows), quantize a per routed row, the down
+ * grouped matmul (o, fp32, sorted rows), the weighted combine into y.
+ *   w1q [E][2I][d], w1_scale [E][2I]; w2q [E][d][I], w2_scale [E][d]
+ * The workspace (w8a8_moe_layer_workspace bytes, 16-byte aligned) holds, at the
+ * offsets w8a8_moe_layer_plan writes to out[0..12]: ids, weights, offsets,
+ * sorted rows, sorted tokens, row-to-sorted, route scratch, xq, x scales, a,
+ * a's codes, a's scales, o.  d % 32 == 0, I % 32 == 0, and the two matmuls'
+ * N conditions above hold.
+ */
+int w8a8_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[13]);
+size_t w8a8_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I);
+int w8a8_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                   const uint8_t* w1q, const float* w1_scale, const uint8_t* w2q, const float* w2_scale,
+                   int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

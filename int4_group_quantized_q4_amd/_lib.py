@@ -63,6 +63,12 @@ SIGNATURES = {
     "w4a16_moe_layer_sorted": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64]),
     "w4a16_moe_layer": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz, _p]),
     "w4a16_moe_layer_noalloc": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p]),
+    "w8a8_quantize_rows": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "w8a8_moe_gmm": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _i32, _p, _i32, _p]),
+    "w8a8_moe_layer_plan": (ctypes.c_int, [_i64, _i32, _i32, _i64, _i64, _p]),
+    "w8a8_moe_layer_workspace": (ctypes.c_size_t, [_i64, _i32, _i32, _i64, _i64]),
+    "w8a8_moe_layer": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p,
+                                      ctypes.c_size_t, _p]),
 }
 
 

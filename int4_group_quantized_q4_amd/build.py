@@ -27,7 +27,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH,
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     # no packed fp32 math (v_pk_*_f32) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

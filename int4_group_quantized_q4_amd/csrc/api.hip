@@ -495,4 +495,146 @@ int w4a16_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, i
                          (size_t)W4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+// ------------------------------------------------------------ FP8 (W8A8)
+
+int w8a8_quantize_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale, hipStream_t stream) {
+  if (rows < 0 || K < 0) return W4_ERR_ARG;
+  if (K % 32 != 0) return W4_ERR_SHAPE;
+  if (rows == 0 || K == 0) return W4_OK;
+  if (rows * K >= ((int64_t)1 << 40)) return W4_ERR_SHAPE;
+  if (!x || !q || !scale) return W4_ERR_ARG;
+  if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scale) & 3u)) return W4_ERR_ARG;
+  w4::launch_fp8_quant_rows(x, rows, K, q, scale, stream);
+  return launch_status();
+}
+
+static int check_fp8_gmm(const w4::Fp8Args& a) {
+  if (a.x_rows < 0 || a.E < 1 || a.E > 256 || a.R < 0 || a.K < 0 || a.N < 0) return W4_ERR_ARG;
+  if (a.epilogue != W4_EPI_NONE && a.epilogue != W4_EPI_GEGLU_TANH && a.epilogue != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  if (a.out_dtype != W4_OUT_BF16 && a.out_dtype != W4_OUT_F32) return W4_ERR_ARG;
+  if (a.epilogue != W4_EPI_NONE && a.out_dtype != W4_OUT_BF16) return W4_ERR_ARG;
+  if (a.K % 32 != 0 || a.N % 16 != 0) return W4_ERR_SHAPE;
+  if (a.R == 0 || a.N == 0) return W4_OK;
+  if (a.K == 0) return W4_ERR_SHAPE;
+  if (!w4::fp8_gemm_supported(a)) return W4_ERR_SHAPE;
+  if (!a.xq || !a.xs || !a.wq || !a.ws || !a.out) return W4_ERR_ARG;
+  if (!a.offsets && a.E != 1) return W4_ERR_ARG;
+  if (!a.row_index && a.x_rows < a.R) return W4_ERR_SHAPE;
+  if (!aligned16(a.xq) || !aligned16(a.wq) || !aligned16(a.out)) return W4_ERR_ARG;
+  return W4_OK;
+}
+
+int w8a8_moe_gmm(const uint8_t* xq, const float* x_scale, int64_t x_rows, const int32_t* row_index,
+                 const int32_t* expert_offsets, int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* wq,
+                 const float* w_scale, int32_t epilogue, void* out, int32_t out_dtype, hipStream_t stream) {
+  w4::Fp8Args a{};
+  a.xq = xq;
+  a.xs = x_scale;
+  a.x_rows = x_rows;
+  a.row_index = row_index;
+  a.offsets = expert_offsets;
+  a.E = E;
+  a.R = R;
+  a.K = K;
+  a.N = N;
+  a.wq = wq;
+  a.ws = w_scale;
+  a.epilogue = epilogue;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  const int st = check_fp8_gmm(a);
+  if (st != W4_OK || R == 0 || N == 0) return st;
+  w4::launch_fp8_gemm(a, stream);
+  return launch_status();
+}
+
+int w8a8_moe_layer_plan(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I, size_t out[13]) {
+  if (!out || T < 0 || E < 1 || E > 256 || k < 1 || k > E || k > 16 || d < 0 || I < 0) return W4_ERR_ARG;
+  const size_t R = (size_t)T * (size_t)k;
+  const size_t sizes[13] = {R * 4, R * 4, (size_t)(E + 1) * 4, R * 4, R * 4, R * 4,
+                            w4::route_workspace_bytes(T, E, k),
+                            (size_t)T * (size_t)d, (size_t)T * 4,
+                            R * (size_t)I * 2, R * (size_t)I, R * 4,
+                            R * (size_t)d * 4};
+  size_t off = 0;
+  for (int i = 0; i < 13; ++i) {
+    out[i] = off;
+    off = align256(off + sizes[i]);
+  }
+  return W4_OK;
+}
+
+size_t w8a8_moe_layer_workspace(int64_t T, int32_t E, int32_t k, int64_t d, int64_t I) {
+  size_t p[13];
+  if (w8a8_moe_layer_plan(T, E, k, d, I, p) != W4_OK) return 0;
+  const size_t R = (size_t)T * (size_t)k;
+  return align256(p[12] + R * (size_t)d * 4);
+}
+
+int w8a8_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t d, int64_t I,
+                   const uint8_t* w1q, const float* w1_scale, const uint8_t* w2q, const float* w2_scale,
+                   int32_t activation, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || k > 16 || d < 0 || I < 0) return W4_ERR_ARG;
+  if (activation != W4_EPI_GEGLU_TANH && activation != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  if (d % 32 != 0 || I % 32 != 0) return W4_ERR_SHAPE;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return W4_ERR_SHAPE;
+  if (T == 0 || d == 0) return W4_OK;
+  if (I == 0) return W4_ERR_SHAPE;
+  if (!x || !logits || !w1q || !w1_scale || !w2q || !w2_scale || !y) return W4_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w1q) || !aligned16(w2q)) return W4_ERR_ARG;
+  const size_t need = w8a8_moe_layer_workspace(T, E, k, d, I);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return W4_ERR_WORKSPACE;
+  size_t p[13];
+  w8a8_moe_layer_plan(T, E, k, d, I, p);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  const int64_t R = T * (int64_t)k;
+  int32_t* ids = reinterpret_cast<int32_t*>(b + p[0]);
+  float* wts = reinterpret_cast<float*>(b + p[1]);
+  int32_t* offs = reinterpret_cast<int32_t*>(b + p[2]);
+  int32_t* srows = reinterpret_cast<int32_t*>(b + p[3]);
+  int32_t* stoks = reinterpret_cast<int32_t*>(b + p[4]);
+  int32_t* r2s = reinterpret_cast<int32_t*>(b + p[5]);
+  uint8_t* xq = b + p[7];
+  float* xs = reinterpret_cast<float*>(b + p[8]);
+  uint16_t* act = reinterpret_cast<uint16_t*>(b + p[9]);
+  uint8_t* aq = b + p[10];
+  float* as = reinterpret_cast<float*>(b + p[11]);
+  float* o = reinterpret_cast<float*>(b + p[12]);
+  w4::Fp8Args a1{}, a2{};
+  a1.xq = xq;
+  a1.xs = xs;
+  a1.x_rows = T;
+  a1.row_index = stoks;
+  a1.offsets = offs;
+  a1.E = a2.E = E;
+  a1.R = a2.R = R;
+  a1.K = d;
+  a1.N = 2 * I;
+  a1.wq = w1q;
+  a1.ws = w1_scale;
+  a1.epilogue = activation;
+  a1.out = act;
+  a1.out_dtype = W4_OUT_BF16;
+  a2.xq = aq;
+  a2.xs = as;
+  a2.x_rows = R;
+  a2.row_index = nullptr;
+  a2.offsets = offs;
+  a2.K = I;
+  a2.N = d;
+  a2.wq = w2q;
+  a2.ws = w2_scale;
+  a2.epilogue = W4_EPI_NONE;
+  a2.out = o;
+  a2.out_dtype = W4_OUT_F32;
+  if (!w4::fp8_gemm_supported(a1) || !w4::fp8_gemm_supported(a2)) return W4_ERR_SHAPE;
+  w4::launch_route(logits, T, E, k, ids, wts, offs, srows, stoks, r2s, b + p[6], stream);
+  w4::launch_fp8_quant_rows(x, T, d, xq, xs, stream);
+  w4::launch_fp8_gemm(a1, stream);
+  w4::launch_fp8_quant_rows(act, R, I, aq, as, stream);
+  w4::launch_fp8_gemm(a2, stream);
+  w4::launch_combine(o, W4_OUT_F32, r2s, wts, T, k, d, y, stream);
+  return launch_status();
+}
+
 }  // extern "C"

@@ -66,4 +66,27 @@ void launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* 
 void launch_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sorted, const float* w,
                     int64_t T, int32_t k, int64_t N, uint16_t* y, hipStream_t stream);
 
+// FP8 (W8A8, E4M3) grouped matmul arguments (dense: E = 1, no offsets).
+struct Fp8Args {
+  const uint8_t* xq;         // [x_rows][K] E4M3 codes
+  const float* xs;           // [x_rows] row scales
+  int64_t x_rows;
+  const int32_t* row_index;  // nullable, [R]
+  const int32_t* offsets;    // nullable, [E+1]
+  int32_t E;
+  int64_t R, K, N;
+  const uint8_t* wq;         // [E][N][K] E4M3 codes
+  const float* ws;           // [E][N] row scales
+  int32_t epilogue;
+  void* out;                 // [R][N] (gated: [R][N/2]) at the sorted rows
+  int32_t out_dtype;
+};
+
+// Rows per expert up to which the FP8 matmul streams weights (else 128-row tiles).
+constexpr int kFp8StreamRowsPerExpert = 32;
+
+bool fp8_gemm_supported(const Fp8Args& a);
+void launch_fp8_gemm(const Fp8Args& a, hipStream_t stream);
+void launch_fp8_quant_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale, hipStream_t stream);
+
 }  // namespace w4

@@ -319,6 +319,76 @@ def w4a16_moe_layer_noalloc(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation,
     check(st, "w4a16_moe_layer_noalloc")
 
 
+# ------------------------------------------------------------- FP8 (W8A8)
+def w8a8_quantize_rows(x, q, scale, stream=None):
+    rows, K = x.shape
+    d = x.device
+    _need(q, "q", rows * K, d)
+    _need(scale, "scale", rows * 4, d)
+    st = lib().w8a8_quantize_rows(_ptr(x, "x", _BF16_LIKE), rows, K, _ptr(q, "q", (torch.uint8,)),
+                                  _ptr(scale, "scale", (torch.float32,)), _stream(stream))
+    check(st, "w8a8_quantize_rows")
+
+
+def w8a8_moe_gmm(xq, x_scale, row_index, expert_offsets, E, R, K, N, wq, w_scale, epilogue, out, out_dtype,
+                 stream=None):
+    _dims(E, R, K, N)
+    if xq.dim() != 2 or xq.shape[1] != K:
+        raise ValueError("xq must be [x_rows, K=%d], got %s" % (K, tuple(xq.shape)))
+    d = xq.device
+    x_rows = xq.shape[0]
+    _need(x_scale, "x_scale", x_rows * 4, d)
+    _need(row_index, "row_index", R * 4, d)
+    _need(expert_offsets, "expert_offsets", (E + 1) * 4, d)
+    _need(wq, "wq", E * N * K, d)
+    _need(w_scale, "w_scale", E * N * 4, d)
+    ncol = N // 2 if epilogue in (W4_EPI_GEGLU_TANH, W4_EPI_SWIGLU) else N
+    if out_dtype == W4_OUT_F32 and out.dtype != torch.float32:
+        raise TypeError("out must be float32 for W4_OUT_F32")
+    if out_dtype == W4_OUT_BF16 and out.dtype not in _BF16_LIKE:
+        raise TypeError("out must be bf16 for W4_OUT_BF16")
+    _need(out, "out", R * ncol * (4 if out_dtype == W4_OUT_F32 else 2), d)
+    st = lib().w8a8_moe_gmm(
+        _ptr(xq, "xq", (torch.uint8,)), _ptr(x_scale, "x_scale", (torch.float32,)), x_rows,
+        _ptr(row_index, "row_index", (torch.int32,), True), _ptr(expert_offsets, "expert_offsets", (torch.int32,), True),
+        E, R, K, N, _ptr(wq, "wq", (torch.uint8,)), _ptr(w_scale, "w_scale", (torch.float32,)), epilogue,
+        _ptr(out, "out", (torch.float32,) + _BF16_LIKE), out_dtype, _stream(stream))
+    check(st, "w8a8_moe_gmm")
+
+
+def w8a8_moe_layer_plan(T, E, k, d, I):
+    arr = (ctypes.c_size_t * 13)()
+    check(lib().w8a8_moe_layer_plan(T, E, k, d, I, arr), "w8a8_moe_layer_plan")
+    return [int(v) for v in arr]
+
+
+def w8a8_moe_layer_workspace(T, E, k, d, I):
+    return int(lib().w8a8_moe_layer_workspace(T, E, k, d, I))
+
+
+def w8a8_moe_layer(x, logits, k, I, w1q, w1_scale, w2q, w2_scale, activation, y, ws, stream=None):
+    T, d = x.shape
+    E = logits.shape[1]
+    _dims(k, I)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError("logits must be [T=%d, E], got %s" % (T, tuple(logits.shape)))
+    dv = x.device
+    _need(logits, "logits", T * E * 4, dv)
+    _need(w1q, "w1q", E * 2 * I * d, dv)
+    _need(w1_scale, "w1_scale", E * 2 * I * 4, dv)
+    _need(w2q, "w2q", E * d * I, dv)
+    _need(w2_scale, "w2_scale", E * d * 4, dv)
+    _need(y, "y", T * d * 2, dv)
+    _need(ws, "ws", 0, dv)
+    wp, wn = _ws(ws)
+    st = lib().w8a8_moe_layer(
+        _ptr(x, "x", _BF16_LIKE), _ptr(logits, "logits", (torch.float32,)), T, E, k, d, I,
+        _ptr(w1q, "w1q", (torch.uint8,)), _ptr(w1_scale, "w1_scale", (torch.float32,)),
+        _ptr(w2q, "w2q", (torch.uint8,)), _ptr(w2_scale, "w2_scale", (torch.float32,)), activation,
+        _ptr(y, "y", _BF16_LIKE), wp, wn, _stream(stream))
+    check(st, "w8a8_moe_layer")
+
+
 # -------------------------------------------------------- allocating helpers
 def repack(w, stream=None):
     """bf16 [rows, K] -> (qweight uint8 [rows*K/2], scales bf16 [rows*K/32]
@@ -408,5 +478,38 @@ def moe_layer(x, logits, k, I, w1_q, w1_s, w2_q, w2_s, activation=W4_EPI_GEGLU_T
         "a": view(7, R * I, torch.bfloat16).view(R, I),
         "o": view(8, R * d, torch.float32).view(R, d),
         "sorted": sorted_path,
+    }
+    return y, views
+
+
+def fp8_moe_layer(x, logits, k, I, w1q, w1_scale, w2q, w2_scale, activation=W4_EPI_GEGLU_TANH, ws=None,
+                  stream=None):
+    """Whole FP8 MoE layer; returns (y, views) with the plan and intermediates."""
+    T, d = x.shape
+    E = logits.shape[1]
+    need = w8a8_moe_layer_workspace(T, E, k, d, I)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    w8a8_moe_layer(x, logits, k, I, w1q, w1_scale, w2q, w2_scale, activation, y, ws, stream)
+    p = w8a8_moe_layer_plan(T, E, k, d, I)
+    R = T * k
+
+    def view(i, n, dt):
+        nbytes = n * torch.empty((), dtype=dt).element_size()
+        return ws[p[i]:p[i] + nbytes].view(dt)
+
+    views = {
+        "topk_ids": view(0, R, torch.int32).view(T, k),
+        "topk_weights": view(1, R, torch.float32).view(T, k),
+        "expert_offsets": view(2, E + 1, torch.int32),
+        "sorted_tokens": view(4, R, torch.int32),
+        "row_to_sorted": view(5, R, torch.int32),
+        "xq": view(7, T * d, torch.uint8).view(T, d),
+        "x_scale": view(8, T, torch.float32),
+        "a": view(9, R * I, torch.bfloat16).view(R, I),
+        "aq": view(10, R * I, torch.uint8).view(R, I),
+        "a_scale": view(11, R, torch.float32),
+        "o": view(12, R * d, torch.float32).view(R, d),
     }
     return y, views

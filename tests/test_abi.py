@@ -231,3 +231,40 @@ def test_noalloc_layer_size_limit_on_host():
     assert L(FAKE, FAKE, 300, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_WORKSPACE
     assert L(FAKE, FAKE, 64, 128, 8, 2816, 700, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_SHAPE
     assert L(FAKE, FAKE, 64, 128, 17, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == w4.W4_ERR_ARG
+
+
+def test_fp8_calls_argument_errors():
+    """The FP8 comparison path's entry points reject bad shapes and pointers on
+    the host, before any launch."""
+    lib = _lib.lib()
+    qr = lib.w8a8_quantize_rows
+    assert qr(FAKE, 4, 48, FAKE, FAKE, None) == w4.W4_ERR_SHAPE       # K % 32
+    assert qr(None, 4, 64, FAKE, FAKE, None) == w4.W4_ERR_ARG
+    assert qr(None, 0, 64, None, None, None) == w4.W4_OK
+    g = lib.w8a8_moe_gmm
+    args = [FAKE, FAKE, 64, FAKE, FAKE, 128, 512, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, w4.W4_OUT_BF16,
+            None]
+    bad = list(args); bad[7] = 2800                  # K % 32
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[8] = 1400                  # N % 16
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[13] = w4.W4_OUT_F32        # gated output is bf16
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[4] = None                  # E > 1 needs offsets
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[9] = None
+    assert g(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[8] = 1392                  # 87 gate tiles... N/32 odd: gated pairs do not split
+    assert g(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[6] = 0                     # R = 0: nothing to do
+    assert g(*bad) == w4.W4_OK
+    ws = lib.w8a8_moe_layer_workspace(64, 128, 8, 2816, 704)
+    R = 64 * 8
+    assert ws >= R * 704 * 3 + R * 2816 * 4 + 64 * 2816
+    plan = (ctypes.c_size_t * 13)()
+    assert lib.w8a8_moe_layer_plan(64, 128, 8, 2816, 704, plan) == w4.W4_OK
+    assert list(plan) == sorted(plan) and all(v % 256 == 0 for v in plan)
+    L = lib.w8a8_moe_layer
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws - 1, None) == w4.W4_ERR_WORKSPACE
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 704, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, ws, None) == w4.W4_ERR_ARG
+    assert L(FAKE, FAKE, 64, 128, 8, 2816, 700, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, ws, None) == w4.W4_ERR_SHAPE
