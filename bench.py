@@ -19,6 +19,8 @@ Workloads (default: moe-decode, with moe-prefill measured in the same run):
                 weights: bit-identical fraction, worst relative difference
   repack        q4_group_repack of 30 layers x 128 experts of on-grid bf16 weights
   e2e           repack of the 30 layers, then T=256 decode through all 30 layers
+  fp8           the moe-decode and moe-prefill layers over FP8 (E4M3) experts, the
+                comparison path (also measured in the default run)
 
 Prints ONE JSON line.  value = touched-expert weight bytes per layer / layer
 time (moe-decode); the roofline object is for the dominant kernel (the gate/up
@@ -360,6 +362,7 @@ def moe_prefill_report(steps, warmup, keep=False):
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
         "gmm1_ms_p10_p90": r["gmm1_ms_p10_p90"],
         "kernel_ms_note": "gmm1 from the timed region; route, gmm2, combine from an instrumented pass after it",
+        "layer_ms_single_call": r["layer_call_ms"],
         "mfma_dtype": "fp16 MFMA on exact s*q weights and fp16 activation rows under a per-row power of two "
                       "(exact bf16 products; fp16 and bf16 share the dense peak)",
         "roofline": {
@@ -418,6 +421,93 @@ def cpu_baseline_decode(layerset):
         "kind": "oracle",
         "sample": "one full moe-decode layer (64 tokens, %d touched experts), NumPy fp64, %.2f s" % (touched, dt),
     }
+
+
+# --------------------------------------------------------------- FP8 (W8A8)
+FP8_MFMA_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, TFLOP/s
+
+
+def fp8_report(steps, warmup, w4_decode_ms=None, w4_prefill_ms=None):
+    """The same MoE layers over FP8 experts (E4M3 codes, fp32 per-channel
+    scales, per-row activation quantization) through w8a8_moe_layer, and the
+    gate/up matmul alone, on the moe-decode and moe-prefill shapes."""
+    dev = torch.device("cuda:0")
+    out = {"workload": "the moe-decode and moe-prefill layers with E4M3 experts (1 byte per weight + fp32 "
+                       "per-row scales), activations quantized per row at run time; w8a8_moe_layer and "
+                       "w8a8_moe_gmm (16x16x128 FP8 MFMA)"}
+    for name, cfg, copies in (("decode", gen.MOE_DECODE, 3), ("prefill", gen.MOE_PREFILL, 3)):
+        T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
+        R = T * k
+        g = gen.torch_generator(dev, 4321 + cfg["id"])
+        layers = []
+        for _ in range(copies):
+            layers.append({"w1q": gen.fp8_codes_t(g, (E * 2 * I * d,), dev), "w1s": gen.fp8_scales_t(g, (E * 2 * I,), dev),
+                           "w2q": gen.fp8_codes_t(g, (E * d * I,), dev), "w2s": gen.fp8_scales_t(g, (E * d,), dev),
+                           "x": gen.bf16_normal_t(g, (T, d), dev),
+                           "logits": gen.router_logits_t(g, T, E, dev, cfg["router"], cfg.get("zipf_s", 1.1))})
+        nws = w4.w8a8_moe_layer_workspace(T, E, k, d, I)
+        wss = [torch.empty(nws, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+
+        def layer(i):
+            L = layers[i % copies]
+            w4.w8a8_moe_layer(L["x"], L["logits"], k, I, L["w1q"], L["w1s"], L["w2q"], L["w2s"],
+                              w4.W4_EPI_GEGLU_TANH, y, wss[i % copies])
+        warm_up(layer, warmup)
+        a, b = TimingEvent(), TimingEvent()
+        a.record()
+        for i in range(steps):
+            layer(i)
+        b.record()
+        torch.cuda.synchronize()
+        layer_ms = a.elapsed_time(b) / steps
+        # gate/up alone on each copy's plan, left in its workspace by the calls above
+        p = w4.w8a8_moe_layer_plan(T, E, k, d, I)
+        views = []
+        for c in range(copies):
+            ws = wss[c]
+            views.append({"offs": ws[p[2]:p[2] + (E + 1) * 4].view(torch.int32),
+                          "stoks": ws[p[4]:p[4] + R * 4].view(torch.int32),
+                          "xq": ws[p[7]:p[7] + T * d].view(T, d),
+                          "xs": ws[p[8]:p[8] + T * 4].view(torch.float32),
+                          "act": ws[p[9]:p[9] + R * I * 2].view(torch.bfloat16).view(R, I)})
+        touched = [int(torch.count_nonzero(v["offs"][1:] - v["offs"][:-1]).item()) for v in views]
+
+        def gmm1(i):
+            L, v = layers[i % copies], views[i % copies]
+            w4.w8a8_moe_gmm(v["xq"], v["xs"], v["stoks"], v["offs"], E, R, d, 2 * I, L["w1q"], L["w1s"],
+                            w4.W4_EPI_GEGLU_TANH, v["act"], w4.W4_OUT_BF16)
+        warm_up(gmm1, warmup)
+        a, b = TimingEvent(), TimingEvent()
+        a.record()
+        for i in range(steps):
+            gmm1(i)
+        b.record()
+        torch.cuda.synchronize()
+        g1_ms = a.elapsed_time(b) / steps
+        mean_touched = float(np.mean([touched[i % copies] for i in range(steps)]))
+        w1b = 2 * I * d + 4 * 2 * I
+        wb = w1b + d * I + 4 * d
+        rep = {"layer_ms": layer_ms, "gmm1_ms": g1_ms, "touched_experts": mean_touched}
+        if name == "decode":
+            rep.update({"weight_bytes_per_layer": mean_touched * wb,
+                        "layer_weight_GBs": mean_touched * wb / (layer_ms * 1e-3) / 1e9,
+                        "gmm1_weight_GBs": mean_touched * w1b / (g1_ms * 1e-3) / 1e9,
+                        "gmm1_frac_of_hbm": mean_touched * w1b / (g1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+            if w4_decode_ms:
+                rep["w4a16_layer_ms"] = w4_decode_ms
+                rep["fp8_over_w4a16_layer_time"] = layer_ms / w4_decode_ms
+        else:
+            f1 = 2.0 * R * d * 2 * I
+            rep.update({"gmm1_TFLOPs": f1 / (g1_ms * 1e-3) / 1e12,
+                        "gmm1_frac_of_fp8_mfma": f1 / (g1_ms * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS,
+                        "layer_TFLOPs": 2.0 * R * d * 3 * I / (layer_ms * 1e-3) / 1e12})
+            if w4_prefill_ms:
+                rep["w4a16_layer_ms"] = w4_prefill_ms
+                rep["fp8_over_w4a16_layer_time"] = layer_ms / w4_prefill_ms
+        out[name] = rep
+        del layers, wss, views
+    return out
 
 
 # ----------------------------------------------------------------- ceilings
@@ -719,7 +809,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="moe-decode",
                     choices=["moe-decode", "moe-prefill", "dense-decode", "dense-prefill", "repack", "repack-export", "e2e",
-                             "copy"])
+                             "copy", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip dense decode, e2e and the ceilings")
@@ -756,6 +846,9 @@ def main():
                                     **dense_decode_report(max(20, args.steps // 2), args.warmup)}
             log("e2e (30-layer repack, then 256-token decode)")
             line["e2e"] = e2e_report(3, 2)
+            log("fp8 comparison")
+            line["fp8"] = fp8_report(max(20, args.steps // 5), args.warmup, rep["layer_ms_single_call"],
+                                     line["prefill"]["layer_ms_single_call"] if "prefill" in line else None)
             log("ceilings")
             line["ceilings"] = ceilings_report()
         if not args.no_cpu_baseline:
@@ -791,6 +884,11 @@ def main():
                      "config": {"workload": "repack-export: one MoE layer (128 experts) exported with fp32 "
                                             "scales and bf16-rounded weights"},
                      "repack": res})
+    elif args.workload == "fp8":
+        res = fp8_report(args.steps, args.warmup)
+        line.update({"value": res["decode"]["layer_weight_GBs"], "unit": "GB/s", "ms_per_step": res["decode"]["layer_ms"],
+                     "dtype": "fp8 e4m3 x e4m3 (fp32 accumulate)",
+                     "config": {"workload": "fp8: moe-decode and moe-prefill layers over E4M3 experts"}, "fp8": res})
     elif args.workload == "copy":
         res = copy_report(args.steps, args.warmup)
         line.update({"value": res["GBs"], "unit": "GB/s", "ms_per_step": res["ms_per_copy"], "dtype": "u8",
