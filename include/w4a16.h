@@ -97,7 +97,9 @@ int w4a16_abi_version(void);
  *   W4_KERNEL_AUTO    (default) by the average rows per expert R/E: up to
  *                     W4_TILED_MIN_ROWS the weight-streaming kernel (every
  *                     weight byte read once per pass of 16 or 32 rows),
- *                     above it the LDS-tiled MFMA kernel;
+ *                     above it the LDS-tiled MFMA kernel; a dense call of at
+ *                     most 16 rows splits K over more waves (one kernel for
+ *                     K <= 4096, else two and the workspace);
  *   W4_KERNEL_STREAM  always the weight-streaming kernel;
  *   W4_KERNEL_TILED   the tiled kernel wherever its shape conditions hold
  *                     (gated: N/32 even; otherwise N % 64 == 0; E <= 256),

@@ -109,8 +109,9 @@ static int run_gemm(const w4::GemmArgs& a, void* ws, size_t ws_bytes, hipStream_
       return W4_ERR_WORKSPACE;
     }
     w4::launch_gemm_tiled(a, ws, stream);
-  } else if (w4::gemm_splitk_supported(a) && ws && aligned16(ws) &&
-             ws_bytes >= w4::gemm_splitk_workspace(a.R, a.K, a.N)) {
+  } else if (policy != W4_KERNEL_STREAM && w4::gemm_splitk_supported(a) &&
+             (!w4::gemm_splitk_needs_workspace(a) ||
+              (ws && aligned16(ws) && ws_bytes >= w4::gemm_splitk_workspace(a.R, a.K, a.N)))) {
     w4::launch_gemm_splitk(a, ws, stream);   // few tiles: split K over more waves
   } else {
     w4::launch_gemm_skinny(a, stream);

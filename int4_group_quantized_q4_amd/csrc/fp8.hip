@@ -52,7 +52,9 @@ constexpr int kBT = kNW * kWT;          // weight tiles per block
 constexpr int kKS = 128;                // K bytes per MFMA step
 constexpr int kAStride = kKS + 16;      // LDS row stride of a staged activation step
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer descriptor word 3 (32-bit data, no swizzle)
-constexpr uint32_t kOOB = 0xFFFFFFF0u;  // a buffer offset past every range: the load returns zeros
+// A buffer offset past every range (ranges stay below 2^31), also after the
+// +16 of a lane's second 16-byte load: such loads return zeros.
+constexpr uint32_t kOOB = 0x80000000u;
 constexpr float kE4M3Max = 448.0f;
 
 // E4M3 x E4M3 -> fp32, 16x16x128; unit block scales (E8M0 127 = 2^0).

@@ -20,6 +20,14 @@
 // codes, a -136 operand for the bias, fp32 scale per group on the VALU).
 // Slices write fp32 partial sums to the workspace; a second kernel adds the
 // slices and rounds.
+//
+// For K <= 4096 (every activation row of the call fits in LDS) one kernel
+// does it all: a workgroup of 16 waves holds 4 weight tiles x 4 K-slices, the
+// activation rows are staged in LDS once, and after the slices' MFMAs the
+// partial sums meet in LDS and are added in slice order (the order of the
+// two-kernel path, so the results are the same bits) and rounded by the
+// slice-0 waves.  No workspace, no second launch, no ordering between
+// workgroups.
 
 #include "common.h"
 #include "internal.h"
@@ -152,6 +160,130 @@ __global__ void __launch_bounds__(64 * kSKWaves) splitk_partial_kernel(GemmArgs 
   }
 }
 
+constexpr int kFTiles = 4;                          // weight tiles per fused workgroup
+constexpr int kFSlices = 4;                         // K-slices per fused workgroup
+constexpr int kFMaxK = 4096;
+constexpr int kFXStride = kFMaxK * 2 + 16;          // LDS row stride of the staged activations
+constexpr int kFMaxBlocks = 8;                      // tile16 blocks per slice at K = 4096
+
+// grid: tile groups of kFTiles; wave wv: tile wv % 4, slice wv / 4; each slice
+// spans sb blocks (the partial block counts as one).
+template <int OUT>
+__global__ void __launch_bounds__(64 * kFTiles * kFSlices) splitk_fused_kernel(GemmArgs a, int sb) {
+  __shared__ __align__(16) uint8_t xs[kMaxRows * kFXStride];
+  __shared__ __align__(16) uint8_t ssc[kFTiles * kFSlices * 1024];   // scale spans, then the partial sums
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int tl = wv % kFTiles, s = wv / kFTiles;
+  const int M = (int)a.R;
+  const int64_t K = a.K, N = a.N;
+  const int G = (int)(K / kGroup);
+  const int NBF = G / kBlockGroups;
+  const int gtail = G - NBF * kBlockGroups;
+  const int tiles = (int)(N / kTileRows);
+  int tile = blockIdx.x * kFTiles + tl;
+  const bool active = tile < tiles;
+  if (!active) tile = tiles - 1;   // idle waves re-read a valid tile and store nothing
+
+  const int kb0 = s * sb;
+  int nb = NBF - kb0 < sb ? NBF - kb0 : sb;   // full blocks of the slice
+  if (nb < 0) nb = 0;
+  const bool tail = gtail > 0 && kb0 <= NBF && NBF < kb0 + sb;   // the partial block is in this slice
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.qweight, 0, (int)(N * K / 2), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)a.scales, 0, (int)(N * G * 2), kRsrcFlags);
+  const uint32_t wtile = (uint32_t)tile * (uint32_t)(8 * K);
+  const uint32_t stile = (uint32_t)tile * (uint32_t)(32 * G);
+
+  // 1. the wave's weight loads: its slice's code blocks (past the last full
+  // block they re-read it), the slice's scale span, the partial block
+  u32x4 cw[kFMaxBlocks];
+  u32x4 sv = {0u, 0u, 0u, 0u};
+  if (nb > 0) {
+#pragma unroll
+    for (int i = 0; i < kFMaxBlocks; ++i) {
+      const int bb = kb0 + (i < nb ? i : nb - 1);
+      cw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wtile + 1024u * bb + 16u * lane, 0, 0));
+    }
+    sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, stile + 128u * kb0 + 16u * lane, 0, 0));
+  }
+  uint32_t ct[3] = {0u, 0u, 0u};
+  float st[3] = {0.f, 0.f, 0.f};
+  if (tail) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < gtail) {
+        ct[j] = __builtin_amdgcn_raw_buffer_load_b32(rw, wtile + 1024u * NBF + 4u * gtail * lane + 4u * j, 0, 0);
+        st[j] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, stile + 128u * NBF + 2u * (r * gtail + j), 0, 0));
+      }
+  }
+
+  // 2. every activation row (rows < M) into LDS, all of K
+  const int ppr = (int)(K / 8);   // 16-byte pieces per row
+  for (int p = (int)threadIdx.x; p < M * ppr; p += 64 * kFTiles * kFSlices) {
+    const int m = p / ppr, pc = p - m * ppr;
+    const int64_t row = a.row_index ? (int64_t)a.row_index[m] : (int64_t)m;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + row * K + 8 * pc);
+    *reinterpret_cast<u32x4*>(xs + m * kFXStride + 16 * pc) = v;
+  }
+  uint8_t* mys = ssc + wv * 1024;
+  *reinterpret_cast<u32x4*>(mys + 16 * lane) = sv;
+  __syncthreads();
+
+  // 3. the slice's blocks: D rows = 4c + i, column = r
+  const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int arow = r < M ? r : 0;   // rows past M read row 0; their results are never stored
+  const uint8_t* xa = xs + arow * kFXStride + (int64_t)kb0 * 256 + c * 16;
+  f32x4 acc = zero4;
+#pragma unroll
+  for (int i = 0; i < kFMaxBlocks; ++i) {
+    if (i >= nb) break;
+    const u32x2 sp = *reinterpret_cast<const u32x2*>(mys + 128 * i + 8 * r);
+    const float sc[4] = {bf16_to_f32(sp[0] & 0xFFFFu), bf16_to_f32(sp[0] >> 16), bf16_to_f32(sp[1] & 0xFFFFu),
+                         bf16_to_f32(sp[1] >> 16)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (i * 4 + j) * 64);
+      const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+      const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(cw[i][j])), cb);
+      acc += sc[j] * p;
+    }
+  }
+  if (tail) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < gtail) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (nb * 4 + j) * 64);
+        const f32x4 cb = mfma16x16x32(A, as_bf16x8(neg136), zero4);
+        const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(ct[j])), cb);
+        acc += st[j] * p;
+      }
+  }
+
+  // 4. the slices' partial sums meet in LDS (the scale spans are done with
+  // once every wave has passed the barrier) and are added in slice order
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(ssc);
+  if (s > 0) red[((s - 1) * kFTiles + tl) * 64 + lane] = acc;
+  __syncthreads();
+  if (s == 0 && active) {
+    f32x4 v = acc;
+#pragma unroll
+    for (int q = 1; q < kFSlices; ++q) v += red[((q - 1) * kFTiles + tl) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * c + i;
+      if (m >= M) continue;
+      const int64_t o = (int64_t)m * N + (int64_t)tile * kTileRows + r;
+      if constexpr (OUT == W4_OUT_F32) static_cast<float*>(a.out)[o] = v[i];
+      else static_cast<uint16_t*>(a.out)[o] = bf16_rne(v[i]);
+    }
+  }
+}
+
 // y[m][n] = sum over slices of part[s][m][n], stored as fp32 or bf16.
 template <int OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nslices, int64_t MN,
@@ -182,7 +314,29 @@ size_t gemm_splitk_workspace(int64_t R, int64_t K, int64_t N) {
   return (size_t)slices_of(K) * (size_t)R * (size_t)N * sizeof(float);
 }
 
+static bool fused_fits(const GemmArgs& a);
+
+bool gemm_splitk_needs_workspace(const GemmArgs& a) { return !fused_fits(a); }
+
+static bool fused_fits(const GemmArgs& a) {
+  const int64_t G = a.K / kGroup;
+  const int64_t nball = (G + kBlockGroups - 1) / kBlockGroups;
+  return a.K <= kFMaxK && (nball + kFSlices - 1) / kFSlices <= kFMaxBlocks;
+}
+
 void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream) {
+  if (fused_fits(a)) {
+    const int64_t G = a.K / kGroup;
+    const int nball = (int)((G + kBlockGroups - 1) / kBlockGroups);
+    const int sb = (nball + kFSlices - 1) / kFSlices;
+    const int groups = (int)((a.N / kTileRows + kFTiles - 1) / kFTiles);
+    const dim3 grid((unsigned)groups), block(64 * kFTiles * kFSlices);
+    if (a.out_dtype == W4_OUT_F32)
+      hipLaunchKernelGGL(splitk_fused_kernel<W4_OUT_F32>, grid, block, 0, stream, a, sb);
+    else
+      hipLaunchKernelGGL(splitk_fused_kernel<W4_OUT_BF16>, grid, block, 0, stream, a, sb);
+    return;
+  }
   const int ns = slices_of(a.K);
   const int tgs = (int)((a.N / kTileRows + kSKWaves - 1) / kSKWaves);
   float* part = static_cast<float*>(ws);

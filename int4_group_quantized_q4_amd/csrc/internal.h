@@ -53,6 +53,8 @@ bool gemm_short_supported(const GemmArgs& a);
 void launch_gemm_short(const GemmArgs& a, hipStream_t stream);
 bool gemm_splitk_supported(const GemmArgs& a);
 size_t gemm_splitk_workspace(int64_t R, int64_t K, int64_t N);
+// false when one kernel does the whole call (K <= 4096): no workspace is used
+bool gemm_splitk_needs_workspace(const GemmArgs& a);
 void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream);
 
 size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);

@@ -100,9 +100,9 @@ def oracle_gmm(xq, xs, row_index, offsets, wq, wsc, epi):
 
 def check(y_gpu, ref, label):
     y = y_gpu.float().cpu().numpy().astype(np.float64)
-    mx, rms = oracle.normwise_errors(y, ref)
+    ok, mx, rms = oracle.within_tolerance(y, ref)
     say("[fp8 gmm] %s max_rel=%.3g rms_rel=%.3g" % (label, mx, rms))
-    assert oracle.within_tolerance(y, ref), (label, mx, rms)
+    assert ok, (label, mx, rms)
 
 
 # (E, counts law, K, N): few rows per expert take the streaming kernel, many the tiled one
@@ -152,8 +152,18 @@ def test_fp8_dense_no_offsets_bf16_out():
 
 
 def layer_case(T, router, label):
+    """The layer stage by stage, each stage against the oracle fed with the
+    GPU's own input to that stage: the per-row quantizations are integer
+    decisions taken from fp32 divisions on both sides (bit-exact), the
+    matmuls and the combine are floating point (normwise tolerance).  The
+    oracle's own end-to-end y is compared too, with a looser bound: the gated
+    activation a is re-quantized to E4M3 per row, and wherever the GPU's a
+    and the oracle's a differ by a bf16 step (fp32 against fp64 sums) at a
+    row's largest element, that row's scale and all its codes move, which
+    is FP8 quantization noise of about 2^-5 relative on those rows."""
     cfg = gen.MOE_DECODE
     E, k, d, I = cfg["E"], cfg["k"], cfg["d"], cfg["I"]
+    R = T * k
     rng = gen.rng_for(953, T)
     x = gen.bf16_normal(rng, (T, d))
     logits = gen.router_logits(rng, T, E, router, 1.1)
@@ -164,17 +174,45 @@ def layer_case(T, router, label):
                                 to_dev(w2q.reshape(-1)), to_dev(w2s.reshape(-1)))
     torch.cuda.synchronize()
     ref = fp8.moe_layer(x, logits, w1q, w1s, w2q, w2s, k=k, keep=True)
-    assert np.array_equal(views["topk_ids"].cpu().numpy(), ref["plan"]["ids"])
+    plan = ref["plan"]
+    assert np.array_equal(views["topk_ids"].cpu().numpy(), plan["ids"])
+    assert np.array_equal(views["expert_offsets"].cpu().numpy(), plan["offsets"])
+    # quantized x: bit-exact
     assert np.array_equal(views["xq"].cpu().numpy(), ref["xq"])
     assert np.array_equal(views["x_scale"].cpu().numpy().view(np.uint32), ref["x_scale"].view(np.uint32))
-    a = oracle.bf16_bits_to_f64(bits_host(views["a"]))
-    mx, rms = oracle.normwise_errors(a, oracle.bf16_bits_to_f64(ref["a"]))
-    say("[fp8 layer] %s a: max_rel=%.3g rms_rel=%.3g" % (label, mx, rms))
-    assert oracle.within_tolerance(a, oracle.bf16_bits_to_f64(ref["a"])), ("a", mx, rms)
+
+    def close(got, want, what):
+        ok, mx, rms = oracle.within_tolerance(got, want)
+        say("[fp8 layer] %s %s: max_rel=%.3g rms_rel=%.3g" % (label, what, mx, rms))
+        assert ok, (what, mx, rms)
+
+    # gate/up with the gated activation, from the (identical) quantized x
+    a_bits = bits_host(views["a"])
+    close(oracle.bf16_bits_to_f64(a_bits), oracle.bf16_bits_to_f64(ref["a"]), "a")
+    # quantized a: bit-exact against the oracle's quantization of the GPU's a
+    aq_ref, as_ref = fp8.quantize_rows(a_bits)
+    aq = views["aq"].cpu().numpy()
+    a_scale = views["a_scale"].cpu().numpy()
+    assert np.array_equal(a_scale.view(np.uint32), as_ref.view(np.uint32))
+    assert np.array_equal(aq, aq_ref)
+    # down matmul from the GPU's quantized a
+    o_ref = np.zeros((R, d))
+    offs = plan["offsets"]
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            o_ref[lo:hi] = fp8.linear(aq[lo:hi], a_scale[lo:hi], w2q[e], w2s[e])
+    o = views["o"].cpu().numpy().astype(np.float64)
+    close(o, o_ref, "o")
+    # combine of the GPU's o
+    from oracle.moe import combine
+    y_ref = combine(o, plan["inv"], plan["weights"])
     yg = oracle.bf16_bits_to_f64(bits_host(y))
-    mx, rms = oracle.normwise_errors(yg, ref["y64"])
-    say("[fp8 layer] %s y: max_rel=%.3g rms_rel=%.3g" % (label, mx, rms))
-    assert oracle.within_tolerance(yg, ref["y64"]), ("y", mx, rms)
+    close(yg, y_ref, "y (combine of the GPU's o)")
+    # end to end against the oracle's own chain
+    ok, mx, rms = oracle.within_tolerance(yg, ref["y64"], 2e-2, 1e-2)
+    say("[fp8 layer] %s y end to end: max_rel=%.3g rms_rel=%.3g" % (label, mx, rms))
+    assert ok, ("y end to end", mx, rms)
 
 
 def test_fp8_layer_decode_full_size():

@@ -99,14 +99,16 @@ def test_linear_empty_M():
 # slice holding only the partial block (K = 1088, 1056), 1..3 tail groups,
 # tile groups with idle waves (N/16 not a multiple of 8), several slices.
 @pytest.mark.parametrize("M,K,N", [(1, 1088, 48), (16, 1056, 32), (7, 4096, 144), (16, 2816, 16),
-                                   (9, 9216, 64), (3, 1120, 128)])
+                                   (9, 9216, 64), (3, 1120, 128), (16, 4096, 14336), (2, 4064, 80),
+                                   (1, 96, 16), (5, 704, 48), (16, 6144, 32)])
 def test_linear_splitk_shapes(M, K, N):
     check_linear(M, K, N, 300 + M + K + N, "split-K %dx%dx%d" % (M, K, N))
 
 
 def test_linear_splitk_agrees_with_streaming():
-    """The same call without a workspace runs the streaming kernel: both match
-    the oracle and each other (they differ in fp32 summation order only)."""
+    """The same call under W4_KERNEL_STREAM runs the streaming kernel: both
+    match the oracle and each other (they differ in fp32 summation order
+    only)."""
     rng = gen.rng_for(920, 9)
     M, K, N = 16, 4096, 256
     packed, sct, codes, sc = linear_weights(rng, N, K)
@@ -114,7 +116,8 @@ def test_linear_splitk_agrees_with_streaming():
     xd, qd, sd = bf16_dev(x), to_dev(packed), bf16_dev(sct)
     y_split = w4.linear(xd, qd, sd, N)
     y_stream = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_linear(xd, qd, sd, N, y_stream)
+    with w4.gemm_kernel(w4.W4_KERNEL_STREAM):
+        w4.w4a16_linear(xd, qd, sd, N, y_stream)
     torch.cuda.synchronize()
     ref = oracle.bf16_bits_to_f64(oracle.linear(x, codes, sc))
     for y in (y_split, y_stream):
@@ -124,3 +127,29 @@ def test_linear_splitk_agrees_with_streaming():
     ok, _, _ = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y_split)),
                                        oracle.bf16_bits_to_f64(bits_host(y_stream)))
     assert ok
+
+
+def test_linear_fused_splitk_matches_two_kernel_sum_order():
+    """K <= 4096 runs the fused split-K kernel (slices summed in LDS in slice
+    order), larger K the two-kernel path (partial sums in the workspace, then
+    a slice-order sum).  The same matrix padded to K = 4128 with zero codes
+    and zero activations has the same four 1024-column slices plus a fifth
+    that adds +0, so the two outputs agree bit for bit."""
+    import layout
+    rng = gen.rng_for(920, 11)
+    M, K, N = 4, 4096, 128
+    codes = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    sc = gen.scales_loguniform(rng, (N, K // 32))
+    x = gen.bf16_normal(rng, (M, K))
+    Kp = K + 32
+    codes_p = np.zeros((N, Kp), dtype=np.int8)
+    codes_p[:, :K] = codes
+    sc_p = np.concatenate([sc, sc[:, :1]], axis=1)
+    x_p = np.zeros((M, Kp), dtype=np.uint16)
+    x_p[:, :K] = x
+    y4k = run_linear(x, layout.encode(codes), layout.encode_scales(sc), N)
+    y_pad = run_linear(x_p, layout.encode(codes_p), layout.encode_scales(sc_p), N)
+    ref = oracle.linear(x, codes, sc)
+    ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(y4k), oracle.bf16_bits_to_f64(ref))
+    assert ok, (mx, rms)
+    assert np.array_equal(y4k, y_pad)
