@@ -293,6 +293,15 @@ def test_moe_layer_small_shapes(cfg):
     check_layer(cfg, "small T=%d" % cfg["T"])
 
 
+@pytest.mark.parametrize("cfg", [dict(id=947, T=256, d=2816, I=704, E=128, k=8, router="normal"),
+                                 dict(id=948, T=160, d=256, I=1056, E=64, k=8, router="normal")])
+def test_moe_layer_sixteen_rows_per_expert(cfg):
+    """About 16 rows per expert on the streaming path, where about half the
+    experts take a second 16-row pass: the 256-token batch of the end-to-end
+    decode at full size, and a long-K down projection (decode kernel)."""
+    assert not check_layer(cfg, "16 rows/expert T=%d" % cfg["T"])
+
+
 @pytest.mark.parametrize("kernel", [w4.W4_KERNEL_AUTO, w4.W4_KERNEL_STREAM])
 def test_moe_layer_prefill_full_size(kernel):
     with w4.gemm_kernel(kernel):
