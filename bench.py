@@ -57,14 +57,14 @@ EXPERT_W2_BYTES = 2816 * 704 // 2 + 2816 * 22 * 2    # 1,115,136
 # csrc/, in order); once one changes, the bench reports traffic as null.
 TRAFFIC = {
     "decode_gmm1": {"sources": ("gemm_skinny.hip", "common.h", "internal.h"),
-                    "sha256": "587082ab59337f91c8ccf5c4aed3a782108b7577db97f36e5fe1b4a763bd30ca",
-                    "read_bytes": 289843200, "write_bytes": 720896},
+                    "sha256": "d4f9d057cf9ba2b1d1aae08b08208d8986c224bbcc73e00b7866952d48239a3e",
+                    "read_bytes": 141219 * 2048, "write_bytes": 704 * 1024},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "4149931c886f0be788a5af5e6593bde80c9516577db858d30127774e074bec06",
-                     "read_bytes": 562426470, "write_bytes": 46152806},
+                     "sha256": "73b554c7da7f18389ddc53f11a7adf873059657938ed3b4c207209c3e4157808",
+                     "read_bytes": 280491 * 2048, "write_bytes": 45076 * 1024},
     "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                      "sha256": "4149931c886f0be788a5af5e6593bde80c9516577db858d30127774e074bec06",
-                      "read_bytes": 1127654810, "write_bytes": 117454848},
+                      "sha256": "73b554c7da7f18389ddc53f11a7adf873059657938ed3b4c207209c3e4157808",
+                      "read_bytes": 550839 * 2048, "write_bytes": 114702 * 1024},
 }
 
 
@@ -670,7 +670,7 @@ def dense_prefill_report(steps, warmup):
             "TFLOPs": tf, "flops_per_call": flops,
             "roofline": {"bound": "mfma", "kernel": "w4a16_linear (prefill GEMM, fp16 MFMA on exact s*q)",
                          "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
-                         "traffic": traffic_of("dense_prefill")}}
+                         "traffic": traffic_of("dense_prefill"), "traffic_source": traffic_source("dense_prefill")}}
 
 
 # ------------------------------------------------------------------- repack
