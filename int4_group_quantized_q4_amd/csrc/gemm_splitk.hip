@@ -197,40 +197,55 @@ __global__ void __launch_bounds__(64 * kFTiles * kFSlices) splitk_fused_kernel(G
   const uint32_t wtile = (uint32_t)tile * (uint32_t)(8 * K);
   const uint32_t stile = (uint32_t)tile * (uint32_t)(32 * G);
 
-  // 1. the wave's weight loads: its slice's code blocks (past the last full
-  // block they re-read it), the slice's scale span, the partial block
+  // 1. every load of the wave, in the order the waits need them (memory
+  // counters drain in issue order), all unconditional so that the compiler
+  // counts them exactly: its pieces of the activation rows, the slice's scale
+  // span, then the code blocks (past the last full block they re-read it)
+  // and the partial block.  The LDS stores below wait for the first two
+  // only, so the blocks are still arriving when the MFMAs start.  Loads that
+  // are not needed get an offset past their descriptor's range and return
+  // zeros.
+  constexpr int kXP = kMaxRows * (kFMaxK / 8) / (64 * kFTiles * kFSlices);   // pieces per thread, at most
+  constexpr uint32_t kOff = 0x80000000u;                                     // past every range
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, (int)(M * K * 2), kRsrcFlags);
+  u32x4 xv[kXP];
+#pragma unroll
+  for (int q = 0; q < kXP; ++q)   // piece p: row p / (K/8), 16 bytes at p*16 (rows are contiguous)
+    xv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rx, 16u * ((uint32_t)threadIdx.x + (uint32_t)(q * 64 * kFTiles * kFSlices)), 0, 0));
+  const u32x4 sv = __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, nb > 0 ? stile + 128u * kb0 + 16u * lane : kOff, 0, 0));
   u32x4 cw[kFMaxBlocks];
-  u32x4 sv = {0u, 0u, 0u, 0u};
-  if (nb > 0) {
 #pragma unroll
-    for (int i = 0; i < kFMaxBlocks; ++i) {
-      const int bb = kb0 + (i < nb ? i : nb - 1);
-      cw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wtile + 1024u * bb + 16u * lane, 0, 0));
-    }
-    sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, stile + 128u * kb0 + 16u * lane, 0, 0));
+  for (int i = 0; i < kFMaxBlocks; ++i) {
+    const int bb = kb0 + (i < nb ? i : nb - 1);
+    cw[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, nb > 0 ? wtile + 1024u * bb + 16u * lane : kOff, 0, 0));
   }
-  uint32_t ct[3] = {0u, 0u, 0u};
-  float st[3] = {0.f, 0.f, 0.f};
-  if (tail) {
+  uint32_t ct[3], stb[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < gtail) {
-        ct[j] = __builtin_amdgcn_raw_buffer_load_b32(rw, wtile + 1024u * NBF + 4u * gtail * lane + 4u * j, 0, 0);
-        st[j] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, stile + 128u * NBF + 2u * (r * gtail + j), 0, 0));
-      }
+  for (int j = 0; j < 3; ++j) {
+    const bool live = tail && j < gtail;
+    ct[j] = __builtin_amdgcn_raw_buffer_load_b32(rw, live ? wtile + 1024u * NBF + 4u * gtail * lane + 4u * j : kOff, 0, 0);
+    stb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? stile + 128u * NBF + 2u * (r * gtail + j) : kOff, 0, 0);
   }
 
-  // 2. every activation row (rows < M) into LDS, all of K
+  // 2. the activation rows (rows < M, all of K) and the scale span into LDS
   const int ppr = (int)(K / 8);   // 16-byte pieces per row
-  for (int p = (int)threadIdx.x; p < M * ppr; p += 64 * kFTiles * kFSlices) {
-    const int m = p / ppr, pc = p - m * ppr;
-    const int64_t row = a.row_index ? (int64_t)a.row_index[m] : (int64_t)m;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + row * K + 8 * pc);
-    *reinterpret_cast<u32x4*>(xs + m * kFXStride + 16 * pc) = v;
+#pragma unroll
+  for (int q = 0; q < kXP; ++q) {
+    const int p = (int)threadIdx.x + q * 64 * kFTiles * kFSlices;
+    if (p < M * ppr) {
+      const int m = p / ppr, pc = p - m * ppr;
+      *reinterpret_cast<u32x4*>(xs + m * kFXStride + 16 * pc) = xv[q];
+    }
   }
   uint8_t* mys = ssc + wv * 1024;
   *reinterpret_cast<u32x4*>(mys + 16 * lane) = sv;
   __syncthreads();
+  float st[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) st[j] = bf16_to_f32(stb[j]);
 
   // 3. the slice's blocks: D rows = 4c + i, column = r
   const u32x4 neg136 = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
@@ -321,7 +336,8 @@ bool gemm_splitk_needs_workspace(const GemmArgs& a) { return !fused_fits(a); }
 static bool fused_fits(const GemmArgs& a) {
   const int64_t G = a.K / kGroup;
   const int64_t nball = (G + kBlockGroups - 1) / kBlockGroups;
-  return a.K <= kFMaxK && (nball + kFSlices - 1) / kFSlices <= kFMaxBlocks;
+  // the fused kernel reads the activation rows as one contiguous block
+  return !a.row_index && a.K <= kFMaxK && (nball + kFSlices - 1) / kFSlices <= kFMaxBlocks;
 }
 
 void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream) {

@@ -153,3 +153,37 @@ def test_linear_fused_splitk_matches_two_kernel_sum_order():
     ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(y4k), oracle.bf16_bits_to_f64(ref))
     assert ok, (mx, rms)
     assert np.array_equal(y4k, y_pad)
+
+
+def test_linear_dense_prefill_with_zero_groups_full_size():
+    """All-zero groups as the repack emits them (codes 0, scale +0: ±0 is
+    outside fp16's exact range for s*q, so every block holding one is redone
+    by the exact kernel) scattered over 1% of the groups of the full
+    prefill-shaped matrix: the exact relaunch at full size, 24 sampled rows
+    against the oracle."""
+    import layout
+    cfg = gen.DENSE_PREFILL
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    rng = gen.rng_for(921, 2)
+    codes = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    sc = gen.scales_loguniform(rng, (N, K // 32))
+    zero = rng.random((N, K // 32)) < 0.01
+    sc[zero] = 0
+    codes.reshape(N, K // 32, 32)[zero] = 0
+    x = gen.bf16_normal(rng, (M, K))
+    xd, qd, sd = bf16_dev(x), to_dev(layout.encode(codes)), bf16_dev(layout.encode_scales(sc))
+    y = w4.linear(xd, qd, sd, N)   # warm-up and result
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    w4.linear(xd, qd, sd, N)
+    t1.record()
+    torch.cuda.synchronize()
+    say("  dense-prefill with %d zero groups: %.0f us per call (every block redone exactly)"
+        % (int(zero.sum()), t0.elapsed_time(t1) * 1e3))
+    yb = bits_host(y)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
+    ref = oracle.linear(x[rows], codes, sc)
+    for i, row in enumerate(rows):
+        ok, mx, rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(yb[row]), oracle.bf16_bits_to_f64(ref[i]))
+        assert ok, (row, mx, rms)
