@@ -538,6 +538,18 @@ def ceilings_report():
     b.record()
     torch.cuda.synchronize()
     stream_gbs = nbytes / (a.elapsed_time(b) / 10 * 1e-3) / 1e9
+    # the same stream over one dense-decode call's weight bytes (33,030,144)
+    small = 33030144
+    sblocks = small // 16 // 4 // 256   # 2016 blocks: every thread issues its 4 loads at once
+    runs = lambda i: lp.w4probe_stream(buf.data_ptr() + (i % 16) * small, small, out.data_ptr(), sblocks, st)
+    warm_up(runs, 20)
+    a, b = TimingEvent(), TimingEvent()
+    a.record()
+    for i in range(200):
+        runs(i)
+    b.record()
+    torch.cuda.synchronize()
+    small_us = a.elapsed_time(b) / 200 * 1e3
     del buf
     mblocks, iters = 256 * 4, 4096
     mout = torch.empty(mblocks * 256, dtype=torch.float32, device=dev)
@@ -552,8 +564,10 @@ def ceilings_report():
     flops = 2.0 * 16 * 16 * 32 * 8 * iters * 4 * mblocks
     mfma_tf = flops / (a.elapsed_time(b) / 5 * 1e-3) / 1e12
     return {"hbm_read_stream_GBs": stream_gbs, "hbm_read_stream_frac_of_peak": stream_gbs / HBM_PEAK_GBS,
+            "read_stream_33MB_us": small_us, "read_stream_33MB_GBs": small / (small_us * 1e-6) / 1e9,
             "mfma_f16_TFLOPs": mfma_tf, "mfma_f16_frac_of_peak": mfma_tf / BF16_MFMA_PEAK_TFLOPS,
-            "note": "read-only stream of 2 GiB (16-byte loads) and register-only fp16 16x16x32 MFMA loops, "
+            "note": "read-only stream of 2 GiB (16-byte loads), the same over 33 MB back to back (one dense-decode "
+                    "call's weight bytes, 16 rotating buffers), and register-only fp16 16x16x32 MFMA loops, "
                     "measured in this run"}
 
 

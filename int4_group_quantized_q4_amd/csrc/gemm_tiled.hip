@@ -32,7 +32,8 @@
 //    expands it in registers: the offset-binary nibble u OR-ed into fp16 1024.0
 //    gives 1024 + u, minus 1032 gives q, times the fp16 scale gives s*q.
 // Gated epilogue: a wave's 4 column tiles are 2 gate tiles and the matching 2
-// up tiles, so act(gate) * up is formed in registers.
+// up tiles, so act(gate) * up is formed in registers; the results leave
+// through LDS as 64-byte row pieces.
 // Padding: an item holding at most 64 rows (an expert's last row tile) runs a
 // copy of the pipeline with MFMAs for 4 row tiles instead of 8, and in a
 // matrix's last column block the waves left without weight tiles skip the
@@ -509,38 +510,82 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         }
       }
     }
+    __syncthreads();   // every wave is done with the staging buffer before the epilogue reuses LDS
   }
 
   if (!active) return;
   // D element q of row tile i: row 16i + 4*(lane/16) + q, weight row lane%16 of
   // each tile; the row's activation exponent undoes the fp16 scaling.  bf16
   // results are rounded to nearest even by the hardware conversion.
+  auto row_exp = [&](int rr) __attribute__((always_inline)) {
+    const int64_t row = row_begin + (rr < cnt ? rr : 0);
+    const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
+    return a.xexp[src];
+  };
+  auto dst_row = [&](int rr) __attribute__((always_inline)) -> int64_t {
+    const int64_t row = row_begin + rr;
+    return a.out_index ? (int64_t)a.out_index[row] : row;
+  };
+  // Gated results go out through LDS (each wave its own 16 KiB ring slot,
+  // free once the loop is done): written there in the MFMA layout, read back
+  // by rows and stored 16 bytes per lane, so a row's 64-byte segment leaves in
+  // one piece instead of as 2-byte stores.  Staged rows are padded to 80 B so
+  // that the four row groups of a wave's writes fall in different banks.
+  uint8_t* eb = wv == 0 ? As0 : (wv == 1 ? As1 : (wv == 2 ? As2 : As3));
+  if constexpr (GATED) {
+    constexpr int GS = 80;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    if (i >= nmt) continue;
+    for (int i = 0; i < MT; ++i) {
+      if (i >= nmt) continue;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rr = 16 * i + 4 * c + q;
-      if (rr >= cnt) continue;
-      const int64_t row = row_begin + rr;
-      const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
-      const int ex = a.xexp[src];
-      const int64_t dst = a.out_index ? (int64_t)a.out_index[row] : row;
-      if constexpr (GATED) {
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + dst * (N / 2) + r;
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 16 * i + 4 * c + q;
+        const int ex = row_exp(rr);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float g = (float)(__bf16)ldexpf(acc[i][t][q], ex);
           const float u = (float)(__bf16)ldexpf(acc[i][t + 2][q], ex);
           const float act = (EPI == W4_EPI_GEGLU_TANH) ? gelu_tanh_f32(g) : silu_f32(g);
-          orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)(act * u));
+          *reinterpret_cast<uint16_t*>(eb + rr * GS + (16 * t + r) * 2) = __builtin_bit_cast(uint16_t, (__bf16)(act * u));
         }
-      } else if constexpr (OUT == W4_OUT_F32) {
-        float* orow = static_cast<float*>(a.out) + dst * N + r;
+      }
+    }
+    // 4 lanes per row (64 bytes: the wave's two gate tiles), 16 rows per store
+    uint16_t* obase = static_cast<uint16_t*>(a.out) + tile[0] * kTileRows + 8 * (lane & 3);
+#pragma unroll
+    for (int k = 0; k < MT; ++k) {
+      const int rr = 16 * k + (lane >> 2);
+      if (rr < cnt) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(eb + rr * GS + 16 * (lane & 3));
+        *reinterpret_cast<u32x4*>(obase + dst_row(rr) * (N / 2)) = v;
+      }
+    }
+  } else if constexpr (OUT == W4_OUT_F32) {
+    // (staged through LDS like the gated case this measured no faster: the
+    // 369 MB of fp32 rows the MoE down matmul writes are bound by their bytes)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= nmt) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 16 * i + 4 * c + q;
+        if (rr >= cnt) continue;
+        const int ex = row_exp(rr);
+        float* orow = static_cast<float*>(a.out) + dst_row(rr) * N + r;
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t) orow[tile[t] * kTileRows] = ldexpf(acc[i][t][q], ex);
-      } else {
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + dst * N + r;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= nmt) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 16 * i + 4 * c + q;
+        if (rr >= cnt) continue;
+        const int ex = row_exp(rr);
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + dst_row(rr) * N + r;
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t)
           orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[i][t][q], ex));
