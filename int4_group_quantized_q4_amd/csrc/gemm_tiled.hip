@@ -387,13 +387,28 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
       }
     }
     // every row tile of the variant, also those past the expert's count
-    // (never stored): straight-line code lets the operand reads run ahead of
-    // the MFMAs
+    // (never stored).  The A operands are read two row tiles at a time, one
+    // pair ahead of the MFMAs that use them, and scheduling barriers keep the
+    // reads there: left to itself the compiler reads each pair right before
+    // its MFMAs and waits out the LDS latency every 8 MFMAs.
+    const uint8_t* ap = Ab + apos;
+    h8 A0 = *reinterpret_cast<const h8*>(ap);
+    h8 A1 = *reinterpret_cast<const h8*>(ap + 16 * AROW);
 #pragma unroll
-    for (int i = 0; i < mtv; ++i) {
-      const h8 A = *reinterpret_cast<const h8*>(Ab + apos + i * 16 * AROW);
+    for (int i = 0; i < mtv; i += 2) {
+      h8 N0 = A0, N1 = A1;
+      if (i + 2 < mtv) {
+        N0 = *reinterpret_cast<const h8*>(ap + (i + 2) * 16 * AROW);
+        N1 = *reinterpret_cast<const h8*>(ap + (i + 3) * 16 * AROW);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A, B[t], acc[i][t]);
+      for (int t = 0; t < WN_TILES; ++t) acc[i][t] = mfma_f16(A0, B[t], acc[i][t]);
+#pragma unroll
+      for (int t = 0; t < WN_TILES; ++t) acc[i + 1][t] = mfma_f16(A1, B[t], acc[i + 1][t]);
+      __builtin_amdgcn_sched_barrier(0);
+      A0 = N0;
+      A1 = N1;
     }
   };
 
