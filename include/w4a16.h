@@ -334,7 +334,12 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
  *   streaming  (at most 64 rows per expert on average and T <= 256; the
  *              default for decode batches) w4a16_moe_topk, w4a16_moe_gmm_ids
  *              for the gate/up (row_div = k) and the down (row_div = 1)
- *              matmuls, then w4a16_moe_combine (row r = t*k + j): no sort;
+ *              matmuls, then w4a16_moe_combine (row r = t*k + j): no sort.
+ *              Up to 64 tokens and 128 experts, when the gate/up matmul runs
+ *              on the one-tile streaming kernel, its workgroups rank the
+ *              logits themselves (descending, ties to the lower id, as
+ *              w4a16_moe_topk) and write the same ids and softmax weights in
+ *              place of the top-k launch;
  *   sorted     the full routing plan of w4a16_moe_route, then the two matmuls
  *              gather their rows through it, then w4a16_moe_combine.
  * Both store the intermediates a and o at the routed rows r = t*k + j.

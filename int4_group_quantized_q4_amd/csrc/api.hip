@@ -413,10 +413,19 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
 
   if (!layer_sorted(a1, a2, T)) {
     // Few rows per expert: no sort.  Each matmul workgroup finds its expert's
-    // rows in the top-k ids (w4a16_moe_topk, w4a16_moe_gmm_ids twice).
-    w4::launch_topk(logits, T, E, k, ids, wts, stream);
-    a1.ids = ids;
+    // rows in the top-k ids (w4a16_moe_topk, w4a16_moe_gmm_ids twice).  Up to
+    // 64 tokens the gate/up workgroups find them from the logits themselves
+    // and write the ids and weights for the down matmul and the combine, in
+    // place of the top-k launch.
     a1.kslots = k;
+    if (w4::gemm_skinny_takes_logits(a1, T, logits)) {
+      a1.logits = logits;
+      a1.ids_out = ids;
+      a1.wts_out = wts;
+    } else {
+      w4::launch_topk(logits, T, E, k, ids, wts, stream);
+      a1.ids = ids;
+    }
     a2.ids = ids;
     a2.kslots = 1;
     w4::launch_gemm_skinny(a1, stream);

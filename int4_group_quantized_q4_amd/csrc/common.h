@@ -164,6 +164,57 @@ __device__ __forceinline__ int expert_rows_from_ids(const int32_t* __restrict__ 
   return total;
 }
 
+// Reductions within each 16-lane row by DPP (every lane gets its row's
+// result), and over the wave from the four rows' results.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_row_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_row_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_row_f32<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_row_f32<0x140>(v));   // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_row_f32<0xB1>(v);
+  v += dpp_row_f32<0x4E>(v);
+  v += dpp_row_f32<0x141>(v);
+  return v + dpp_row_f32<0x140>(v);
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// wave-uniform maximum
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+// wave-uniform sum, as (row0 + row1) + (row2 + row3)
+__device__ __forceinline__ float wave_sum_all(float v) {
+  v = row16_sum(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+
+// Softmax terms of one token whose logits sit S per lane (lane l holds experts
+// l, l + 64, ...; live[s] false past E): the token's largest logit mx and
+// sum_e exp(l_e - mx), both wave-uniform.  The routing kernel and the
+// logits-mode decode matmul both take them from here, so the routing weights
+// they write agree bit for bit.
+template <int S>
+__device__ __forceinline__ void token_softmax_terms(const float v[S], const bool live[S], float& mx, float& sum) {
+  float cand = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (live[s]) cand = fmaxf(cand, v[s]);
+  mx = wave_max_all(cand);
+  sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (live[s]) sum += expf(v[s] - mx);
+  sum = wave_sum_all(sum);
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -54,15 +54,86 @@ __device__ __forceinline__ int xcd_item(int b, int total) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// ---- Rows from the router logits (T <= 64 tokens, E <= 128 experts,
+// finite logits).  Token t sends a row to expert e in slot j =
+// the number of its logits above l[t][e], equal logits of lower ids counted
+// as above, when j < k: the top-k order of the routing kernel (descending
+// logit, ties to the lower id), so routed row r = t*k + j is the row that
+// kernel's ids would give.
+constexpr int kLogitsMaxTokens = 64;
+constexpr int kLogitsMaxExperts = 128;
+constexpr int kLogitsPerWave = kLogitsMaxTokens / kWaves;   // tokens ranked per wave
+
+// Wave w ranks tokens w, w + 8, ...; lg[i][s] holds the i-th one's logits of
+// experts lane + 64 s (-inf past E or T).
+__device__ __forceinline__ void logits_batch(const float* __restrict__ logits, int T, int E,
+                                             float lg[kLogitsPerWave][2]) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < kLogitsPerWave; ++i) {
+    const int t = wv + kWaves * i;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int x = lane + 64 * s;
+      lg[i][s] = (t < T && x < E) ? logits[(int64_t)t * E + x] : -INFINITY;
+    }
+  }
+}
+
+// Expert e's routed rows, in increasing r, to rows[0 .. count); returns count.
+// The expert's plan entries (ids and softmax weights at t*k + j) are written
+// by workgroup part = t % nparts of the expert's nparts workgroups (ids_out
+// null: none).  s_rank: 64 ints of LDS.  Ends with a workgroup barrier.
+__device__ __forceinline__ int expert_rows_from_logits(const float lg[kLogitsPerWave][2], int T, int E, int k, int e,
+                                                       int* rows, int* s_rank, int* s_cnt, int part, int nparts,
+                                                       int32_t* __restrict__ ids_out, float* __restrict__ wts_out) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool live[2] = {lane < E, lane + 64 < E};
+#pragma unroll
+  for (int i = 0; i < kLogitsPerWave; ++i) {
+    const int t = wv + kWaves * i;
+    if (t >= T) break;   // wave-uniform
+    const float held = e >= 64 ? lg[i][1] : lg[i][0];   // (e is uniform)
+    const float le = lane_f32(held, e & 63);
+    const bool a0 = lg[i][0] > le || (lg[i][0] == le && lane < e);
+    const bool a1 = lg[i][1] > le || (lg[i][1] == le && lane + 64 < e);
+    const int j = __popcll(__ballot(a0)) + __popcll(__ballot(a1));
+    if (lane == 0) s_rank[t] = j;
+    if (ids_out && j < k && t % nparts == part) {   // wave-uniform
+      float mx, sum;
+      token_softmax_terms<2>(lg[i], live, mx, sum);
+      if (lane == 0) {
+        ids_out[(int64_t)t * k + j] = e;
+        wts_out[(int64_t)t * k + j] = expf(le - mx) / sum;
+      }
+    }
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int j = lane < T ? s_rank[lane] : k;
+    const uint64_t b = __ballot(j < k);
+    const int pos = __popcll(b & ((1ull << lane) - 1ull));
+    if (j < k) rows[pos] = lane * k + j;
+    if (lane == 0) s_cnt[0] = __popcll(b);
+  }
+  __syncthreads();
+  return s_cnt[0];
+}
 
 // D: code/scale blocks in flight per wave (ring depth); a chunk of staged
 // activations spans max(4, D) blocks so that ring slots are compile-time.
-// IDS: rows from the top-k ids (GemmArgs::ids): activation row r / kslots,
-// output row r.
-template <int MAXT, int EPI, int OUT, int D, bool IDS>
+// RM (row mode) 0: rows from the expert offsets (optionally gathered);
+// 1: routed rows r from the top-k ids (GemmArgs::ids), activation row
+// r / kslots, output row r; 2: the same routed rows found from the router
+// logits (GemmArgs::logits), the expert's workgroups writing the expert's
+// entries of the top-k plan (ids_out, wts_out) between them.
+template <int MAXT, int EPI, int OUT, int D, int RM>
 __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmArgs a, int wg_per_expert,
                                                                            int total_wg, int units_per_expert) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
+  constexpr bool IDS = RM != 0;
   constexpr int CB = D > 4 ? D : 4;       // blocks per staged activation chunk
   constexpr int KC = CB * 128;            // columns per chunk
   constexpr int XS = KC * 2 + 16;         // LDS row stride in bytes (padded off the bank period)
@@ -123,16 +194,25 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   // in their own prologue, after the barrier that ends the previous pass.
   // (The ids go out first: the scan must not wait for the ring to land.)
   int idv[8];
-  if constexpr (IDS) {
+  float lgv[RM == 2 ? kLogitsPerWave : 1][2];
+  const int ntok = (int)a.R / a.kslots;   // (logits mode: R <= 64 k)
+  if constexpr (RM == 1) {
     if (a.R > 512 || wv == 0) ids_batch(a.ids, (int)a.R, wv, idv);
+  } else if constexpr (RM == 2) {
+    logits_batch(a.logits, ntok, a.E, lgv);
   }
   if (NBF > 0) {
 #pragma unroll
     for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
   }
-  if constexpr (IDS) {
+  if constexpr (RM == 1) {
     row_end = __builtin_amdgcn_readfirstlane(
         expert_rows_from_ids<kWaves>(a.ids, (int)a.R, e, s_rows, kIdsMaxExpertRows, s_wcnt, idv));
+  } else if constexpr (RM == 2) {
+    // rows at s_rows[0, 64), ranks staged at s_rows[64, 128)
+    row_end = __builtin_amdgcn_readfirstlane(expert_rows_from_logits(lgv, ntok, a.E, a.kslots, e, s_rows,
+                                                                     s_rows + kLogitsMaxTokens, s_wcnt, wgi,
+                                                                     wg_per_expert, a.ids_out, a.wts_out));
   } else if (a.offsets) {
     row_begin = a.offsets[e];
     row_end = a.offsets[e + 1];
@@ -422,7 +502,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   }
 }
 
-template <int MAXT, int D, bool IDS>
+template <int MAXT, int D, int IDS>
 void launch_m_ids(const GemmArgs& a, hipStream_t stream) {
   const bool gated = a.epilogue != W4_EPI_NONE;
   const int units = (int)(gated ? a.N / 32 : a.N / 16);
@@ -446,25 +526,52 @@ void launch_m_ids(const GemmArgs& a, hipStream_t stream) {
 
 template <int MAXT, int D>
 void launch_m(const GemmArgs& a, hipStream_t stream) {
-  if (a.ids) launch_m_ids<MAXT, D, true>(a, stream);
-  else launch_m_ids<MAXT, D, false>(a, stream);
+  if constexpr (MAXT == 1 && D == kDecodeRing) {
+    if (a.logits) {
+      // (gated only: gemm_skinny_takes_logits)
+      const int units = (int)(a.N / 32);
+      const int wg_per_expert = (units + kWaves / 2 - 1) / (kWaves / 2);
+      const int total = wg_per_expert * a.E;
+      if (a.epilogue == W4_EPI_GEGLU_TANH)
+        hipLaunchKernelGGL((decode_kernel<1, W4_EPI_GEGLU_TANH, W4_OUT_BF16, kDecodeRing, 2>), dim3(total),
+                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units);
+      else
+        hipLaunchKernelGGL((decode_kernel<1, W4_EPI_SWIGLU, W4_OUT_BF16, kDecodeRing, 2>), dim3(total),
+                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units);
+      return;
+    }
+  }
+  if (a.ids) launch_m_ids<MAXT, D, 1>(a, stream);
+  else launch_m_ids<MAXT, D, 0>(a, stream);
+}
+
+// avg rows per expert, short-K eligibility and ring depth -> which kernel
+enum class SkinnyPath { kShort, kM1Deep, kM1, kM2Deep, kM2 };
+SkinnyPath skinny_path(const GemmArgs& a) {
+  const int64_t tiles = (a.N / 16) * a.E;
+  const int64_t avg = (a.R + a.E - 1) / a.E;   // rows per expert: 16-row MFMA tiles per pass
+  const bool deep = tiles < 4096;              // fewer waves than SIMDs need a deeper register ring
+  if (avg <= 16 && gemm_short_supported(a)) return SkinnyPath::kShort;
+  if (avg <= 16) return deep ? SkinnyPath::kM1Deep : SkinnyPath::kM1;
+  return deep ? SkinnyPath::kM2Deep : SkinnyPath::kM2;
 }
 
 }  // namespace
 
+bool gemm_skinny_takes_logits(const GemmArgs& a, int64_t T, const float* logits) {
+  return a.epilogue != W4_EPI_NONE && a.offsets == nullptr && a.row_index == nullptr && T >= 1 &&
+         T <= kLogitsMaxTokens && a.E >= 1 && a.E <= kLogitsMaxExperts && logits != nullptr &&
+         a.kslots >= 1 && a.R == T * a.kslots &&
+         skinny_path(a) == SkinnyPath::kM1;
+}
+
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  // Fewer waves than SIMDs need a deeper register ring to keep HBM busy.
-  const int64_t tiles = (a.N / 16) * a.E;
-  const int64_t avg = (a.R + a.E - 1) / a.E;   // rows per expert: 16-row MFMA tiles per pass
-  const bool deep = tiles < 4096;
-  if (avg <= 16 && gemm_short_supported(a)) {
-    launch_gemm_short(a, stream);   // K <= 1024: several whole tiles per wave
-  } else if (avg <= 16) {
-    if (deep) launch_m<1, 16>(a, stream);
-    else launch_m<1, kDecodeRing>(a, stream);
-  } else {
-    if (deep) launch_m<2, 8>(a, stream);
-    else launch_m<2, kDecodeRing>(a, stream);
+  switch (skinny_path(a)) {
+    case SkinnyPath::kShort: launch_gemm_short(a, stream); break;   // K <= 1024: several whole tiles per wave
+    case SkinnyPath::kM1Deep: launch_m<1, 16>(a, stream); break;
+    case SkinnyPath::kM1: launch_m<1, kDecodeRing>(a, stream); break;
+    case SkinnyPath::kM2Deep: launch_m<2, 8>(a, stream); break;
+    case SkinnyPath::kM2: launch_m<2, kDecodeRing>(a, stream); break;
   }
 }
 

@@ -39,6 +39,13 @@ struct GemmArgs {
   // and its output row is r.  R = T * k routed rows, at most kIdsMaxRows.
   const int32_t* ids;
   int32_t kslots;
+  // Rows from the router logits [R / kslots][E] instead (decode workgroups of
+  // gated matmuls only, see gemm_skinny_takes_logits): the routed rows are
+  // those of the top-k ids, which the call writes to ids_out and the softmax
+  // weights to wts_out ([R], slot order), as the routing kernel would.
+  const float* logits;
+  int32_t* ids_out;
+  float* wts_out;
 };
 
 // Most routed rows of an ids-mode call (an expert holds at most T of them).
@@ -46,6 +53,10 @@ constexpr int kIdsMaxRows = 4096;
 constexpr int kIdsMaxExpertRows = 256;
 
 void launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+// true when launch_gemm_skinny(a) can take its rows from router logits
+// [T][E] at `logits` (a gated matmul on the one-tile streaming kernel,
+// T <= 64, E <= 128)
+bool gemm_skinny_takes_logits(const GemmArgs& a, int64_t T, const float* logits);
 bool gemm_tiled_supported(const GemmArgs& a);
 size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N);
 void launch_gemm_tiled(const GemmArgs& a, void* ws, hipStream_t stream);

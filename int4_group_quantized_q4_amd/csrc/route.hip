@@ -32,30 +32,6 @@ constexpr int kChunkThreads = 256;  // routed rows per ranking chunk
 constexpr int kSmallRows = 4096;    // single-workgroup sort up to this many rows
 constexpr int kSmallThreads = 1024;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Maximum over the wave, returned to every lane.
-__device__ __forceinline__ float wave_max_all(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror: every lane holds its row's max
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
 // Token t on one wave: ids[t][0..k) by descending logit (ties: lower id
 // first) and their softmax probabilities.  E <= 64*S <= 256, k <= E, finite
 // logits.
@@ -78,13 +54,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     for (int s = 0; s < S; ++s)
       if (live[s] && !((taken >> s) & 1u)) cand = fmaxf(cand, v[s]);
     const float m = wave_max_all(cand);
-    if (j == 0) {
-      mx = m;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        if (live[s]) sum += expf(v[s] - mx);
-      sum = wave_sum(sum);
-    }
+    if (j == 0) token_softmax_terms<S>(v, live, mx, sum);
     int sel = -1;
 #pragma unroll
     for (int s = 0; s < S; ++s) {

@@ -241,9 +241,15 @@ def moe_inputs(cfg, seed_base=0):
     return x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s)
 
 
-def check_layer(cfg, label):
+def check_layer(cfg, label, ties=False):
     T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
     x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s) = moe_inputs(cfg)
+    if ties:
+        logits[0, :] = 0.5                               # a row of ties: ids 0..k-1
+        if T > 5:
+            logits[3, E // 2] = logits[3, 1]
+            logits[2, :] = np.round(logits[2, :])            # many ties
+            logits[5:, :] = np.round(logits[5:, :] * 4) / 4  # ties in every row
     say("[moe layer] %s T=%d" % (label, T))
     y, views = w4.moe_layer(bf16_dev(x), to_dev(logits), k, I, to_dev(w1p), bf16_dev(w1t), to_dev(w2p),
                             bf16_dev(w2t), w4.W4_EPI_GEGLU_TANH)
@@ -278,6 +284,17 @@ def test_moe_layer_decode_both_paths(kernel):
     cfg = dict(gen.MOE_DECODE, id=942)
     with w4.gemm_kernel(kernel):
         assert check_layer(cfg, "moe-decode kernel=%d" % kernel) == (kernel == w4.W4_KERNEL_TILED)
+
+
+@pytest.mark.parametrize("T", [1, 40, 64])
+def test_moe_layer_rows_from_logits_with_ties(T):
+    """Up to 64 tokens on the one-tile streaming kernel (K = d above the
+    short kernel's limit, at least 4096 weight tiles) the gate/up workgroups
+    rank the logits themselves instead of reading top-k ids, and write the
+    ids and weights.  Ties between logits must resolve to the lower expert
+    id, as in the routing kernel."""
+    cfg = dict(id=949, T=T, d=1536, I=256, E=128, k=8, router="normal")
+    assert not check_layer(cfg, "rows from logits, ties", ties=True)
 
 
 @pytest.mark.parametrize("cfg", [dict(id=940, T=19, d=96, I=64, E=8, k=3, router="normal"),
