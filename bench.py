@@ -126,9 +126,10 @@ class MoeLayerSet:
         self.y = torch.empty(T, d, dtype=torch.bfloat16, device=device)
         gws = max(w4.w4a16_moe_gmm_workspace(T, R, E, d, 2 * I), w4.w4a16_moe_gmm_workspace(R, R, E, I, d))
         self.gws = torch.empty(max(16, gws), dtype=torch.uint8, device=device)
-        # decode batches take the streaming path of w4a16_moe_layer: top-k, the
-        # two matmuls over rows found from the ids (a and o at the routed rows),
-        # the combine with the identity row map
+        # decode batches take the streaming path of w4a16_moe_layer: the gate/up
+        # matmul with the top-k from the logits, the down matmul over rows
+        # found from the ids (a and o at the routed rows), the combine with the
+        # identity row map
         self.streaming = not w4.w4a16_moe_layer_sorted(T, E, k, d, I)
         self.ident = torch.arange(R, dtype=torch.int32, device=device)
 
@@ -165,11 +166,12 @@ class MoeLayerSet:
         full = ev is not None and len(ev) == 5
         if full:
             ev[0].record()
-        w4.w4a16_moe_topk(L["logits"], k, self.ids, self.wts)
+        # (the top-k plan comes out of the gate/up call: up to 64 tokens its
+        # workgroups rank the logits themselves, else it launches the top-k)
         if ev is not None:
             ev[1 if full else 0].record()
-        w4.w4a16_moe_gmm_ids(L["x"], self.ids, T, k, k, E, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
-                             self.act, w4.W4_OUT_BF16)
+        w4.w4a16_moe_gmm_logits(L["x"], L["logits"], k, d, 2 * I, L["w1q"], L["w1s"], w4.W4_EPI_GEGLU_TANH,
+                                self.act, self.ids, self.wts)
         if ev is not None:
             ev[2 if full else 1].record()
         w4.w4a16_moe_gmm_ids(self.act, self.ids, T, k, 1, E, I, d, L["w2q"], L["w2s"], w4.W4_EPI_NONE, self.o,
@@ -326,12 +328,14 @@ def moe_decode_report(steps, warmup):
         "touched_experts": r["touched_experts"],
         "kernel_ms": {k: round(r[k], 5) for k in ("route_ms", "gmm1_ms", "gmm2_ms", "combine_ms")},
         "gmm1_ms_p10_p90": r["gmm1_ms_p10_p90"],
-        "kernel_ms_note": "gmm1 from the timed region; route (top-k only: the matmuls find their rows in "
-                          "the ids), gmm2, combine from an instrumented pass after it",
+        "kernel_ms_note": "gmm1 (the gate/up matmul, whose workgroups also rank the logits and write the "
+                          "top-k plan) from the timed region; route (no launch of its own on this path), gmm2, "
+                          "combine from an instrumented pass after it",
         "layer_ms_single_call": r["layer_call_ms"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "gate/up grouped matmul (w4a16_moe_gmm, GEGLU epilogue)",
+            "kernel": "gate/up grouped matmul with its rows and the top-k plan from the router logits "
+                      "(w4a16_moe_gmm_logits, GEGLU epilogue)",
             "achieved": w1bytes / (r["gmm1_ms"] * 1e-3) / 1e9,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

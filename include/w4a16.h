@@ -278,6 +278,28 @@ int w4a16_moe_gmm_ids(const uint16_t* x, const int32_t* topk_ids, int64_t T, int
                       void* out, int32_t out_dtype, hipStream_t stream);
 
 /*
+ * w4a16_moe_gmm_logits -- the gate/up matmul of a decode batch with its rows
+ * taken from the router logits: the routed rows of the top-k plan of
+ * w4a16_moe_topk (descending logit, ties to the lower id), each with x row
+ * t, through a gated epilogue:
+ *     out[t*k + j][.] = epilogue(x[t] . W_e^T),  e = the j-th expert of token t
+ * and topk_ids / topk_weights written as w4a16_moe_topk writes them.  Up to
+ * 64 tokens and 128 experts, when the matmul runs on the one-tile streaming
+ * kernel, its workgroups rank the logits themselves (no top-k launch);
+ * otherwise this is w4a16_moe_topk followed by w4a16_moe_gmm_ids (row_div k).
+ * This is the first half of the streaming path of w4a16_moe_layer.
+ *   x          in  [T][K] bf16;  logits in [T][E] fp32 (finite)
+ *   qweight, scales  as in w4a16_moe_gmm (N = 2 x the gated width)
+ *   epilogue   W4_EPI_GEGLU_TANH or W4_EPI_SWIGLU
+ *   out        out [T*k][N/2] bf16
+ *   topk_ids   out [T][k] int32;  topk_weights out [T][k] fp32
+ * Limits of w4a16_moe_topk and w4a16_moe_gmm_ids.
+ */
+int w4a16_moe_gmm_logits(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t K, int64_t N,
+                         const uint8_t* qweight, const uint16_t* scales, int32_t epilogue, uint16_t* out,
+                         int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/*
  * w4a16_moe_gmm -- grouped W4A16 matmul over expert row ranges.
  *
  * The grouped matmul with one scale per 32-wide group that dequantizes each
@@ -332,14 +354,10 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
  * the packed int4 experts and their 32-wide group scales go straight to the
  * grouped matmul.  Two paths, by w4a16_moe_layer_sorted():
  *   streaming  (at most 64 rows per expert on average and T <= 256; the
- *              default for decode batches) w4a16_moe_topk, w4a16_moe_gmm_ids
- *              for the gate/up (row_div = k) and the down (row_div = 1)
- *              matmuls, then w4a16_moe_combine (row r = t*k + j): no sort.
- *              Up to 64 tokens and 128 experts, when the gate/up matmul runs
- *              on the one-tile streaming kernel, its workgroups rank the
- *              logits themselves (descending, ties to the lower id, as
- *              w4a16_moe_topk) and write the same ids and softmax weights in
- *              place of the top-k launch;
+ *              default for decode batches) w4a16_moe_gmm_logits for the
+ *              gate/up matmul (top-k and rows from the logits),
+ *              w4a16_moe_gmm_ids for the down matmul (row_div = 1), then
+ *              w4a16_moe_combine (row r = t*k + j): no sort;
  *   sorted     the full routing plan of w4a16_moe_route, then the two matmuls
  *              gather their rows through it, then w4a16_moe_combine.
  * Both store the intermediates a and o at the routed rows r = t*k + j.

@@ -54,6 +54,7 @@ SIGNATURES = {
     "w4a16_moe_route": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "w4a16_moe_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _p, _p, _p]),
     "w4a16_moe_gmm_ids": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _p, _p, _i32, _p, _i32, _p]),
+    "w4a16_moe_gmm_logits": (ctypes.c_int, [_p, _p, _i64, _i32, _i32, _i64, _i64, _p, _p, _i32, _p, _p, _p, _p]),
     "w4a16_moe_gmm_workspace": (ctypes.c_size_t, [_i64, _i64, _i32, _i64, _i64]),
     "w4a16_moe_gmm": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _i32, _p, _i32, _p,
                                      ctypes.c_size_t, _p]),

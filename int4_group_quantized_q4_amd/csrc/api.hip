@@ -231,6 +231,53 @@ int w4a16_moe_gmm_ids(const uint16_t* x, const int32_t* topk_ids, int64_t T, int
   return launch_status();
 }
 
+// The gate/up matmul of the streaming path from the logits: its workgroups
+// rank the logits when the one-tile streaming kernel takes it (up to 64
+// tokens), else the top-k launch and the ids-mode matmul.  a: the ids-mode
+// arguments without ids (x_rows = T, R = T*k, kslots = k).
+static void enqueue_gateup_from_logits(w4::GemmArgs a, const float* logits, int64_t T, int32_t E, int32_t k,
+                                       int32_t* ids, float* wts, hipStream_t stream) {
+  a.kslots = k;
+  if (w4::gemm_skinny_takes_logits(a, T, logits)) {
+    a.logits = logits;
+    a.ids_out = ids;
+    a.wts_out = wts;
+  } else {
+    w4::launch_topk(logits, T, E, k, ids, wts, stream);
+    a.ids = ids;
+  }
+  w4::launch_gemm_skinny(a, stream);
+}
+
+int w4a16_moe_gmm_logits(const uint16_t* x, const float* logits, int64_t T, int32_t E, int32_t k, int64_t K, int64_t N,
+                         const uint8_t* qweight, const uint16_t* scales, int32_t epilogue, uint16_t* out,
+                         int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  if (epilogue != W4_EPI_GEGLU_TANH && epilogue != W4_EPI_SWIGLU) return W4_ERR_ARG;
+  int st = check_gmm_ids(x, topk_ids, T, k, E, K, N, qweight, scales, out);
+  if (st != W4_OK) return st;
+  if (N % 32 != 0) return W4_ERR_SHAPE;
+  if (T == 0) return W4_OK;
+  if (!logits || !topk_ids || !topk_weights) return W4_ERR_ARG;
+  if (N == 0) {   // no matmul, but the plan is still an output
+    w4::launch_topk(logits, T, E, k, topk_ids, topk_weights, stream);
+    return launch_status();
+  }
+  w4::GemmArgs a{};
+  a.x = x;
+  a.x_rows = T;
+  a.E = E;
+  a.R = T * k;
+  a.K = K;
+  a.N = N;
+  a.qweight = qweight;
+  a.scales = scales;
+  a.epilogue = epilogue;
+  a.out = out;
+  a.out_dtype = W4_OUT_BF16;
+  enqueue_gateup_from_logits(a, logits, T, E, k, topk_ids, topk_weights, stream);
+  return launch_status();
+}
+
 int w4a16_moe_gmm(const uint16_t* x, int64_t x_rows, const int32_t* row_index, const int32_t* expert_offsets,
                   int32_t E, int64_t R, int64_t K, int64_t N, const uint8_t* qweight, const uint16_t* scales,
                   int32_t epilogue, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
@@ -412,23 +459,13 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
   a2.out_dtype = W4_OUT_F32;
 
   if (!layer_sorted(a1, a2, T)) {
-    // Few rows per expert: no sort.  Each matmul workgroup finds its expert's
-    // rows in the top-k ids (w4a16_moe_topk, w4a16_moe_gmm_ids twice).  Up to
-    // 64 tokens the gate/up workgroups find them from the logits themselves
-    // and write the ids and weights for the down matmul and the combine, in
-    // place of the top-k launch.
-    a1.kslots = k;
-    if (w4::gemm_skinny_takes_logits(a1, T, logits)) {
-      a1.logits = logits;
-      a1.ids_out = ids;
-      a1.wts_out = wts;
-    } else {
-      w4::launch_topk(logits, T, E, k, ids, wts, stream);
-      a1.ids = ids;
-    }
+    // Few rows per expert: no sort (w4a16_moe_gmm_logits, w4a16_moe_gmm_ids,
+    // w4a16_moe_combine).  Each matmul workgroup finds its expert's rows in
+    // the top-k ids, or (gate/up, up to 64 tokens) from the logits, writing
+    // the ids and weights for the down matmul and the combine.
+    enqueue_gateup_from_logits(a1, logits, T, E, k, ids, wts, stream);
     a2.ids = ids;
     a2.kslots = 1;
-    w4::launch_gemm_skinny(a1, stream);
     w4::launch_gemm_skinny(a2, stream);
     w4::launch_combine(o, W4_OUT_F32, nullptr, wts, T, k, d, y, stream);
     return launch_status();

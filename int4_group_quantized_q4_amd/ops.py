@@ -206,6 +206,30 @@ def w4a16_moe_gmm_ids(x, topk_ids, T, k, row_div, E, K, N, qweight, scales, epil
     check(st, "w4a16_moe_gmm_ids")
 
 
+def w4a16_moe_gmm_logits(x, logits, k, K, N, qweight, scales, epilogue, out, topk_ids, topk_weights, stream=None):
+    """Gate/up matmul of a decode batch with its rows (and the top-k plan,
+    written to topk_ids / topk_weights) from the router logits [T][E]."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    _dims(T, E, k, K, N)
+    if x.dim() != 2 or x.shape[0] != T or x.shape[1] != K:
+        raise ValueError("x must be [T=%d, K=%d], got %s" % (T, K, tuple(x.shape)))
+    d = x.device
+    _need(logits, "logits", T * E * 4, d)
+    _need(qweight, "qweight", E * N * K // 2, d)
+    _need(scales, "scales", E * N * K // 32 * 2, d)
+    _need(out, "out", T * k * (N // 2) * 2, d)
+    _need(topk_ids, "topk_ids", T * k * 4, d)
+    _need(topk_weights, "topk_weights", T * k * 4, d)
+    st = lib().w4a16_moe_gmm_logits(
+        _ptr(x, "x", _BF16_LIKE), _ptr(logits, "logits", (torch.float32,)), T, E, k, K, N,
+        _ptr(qweight, "qweight", (torch.uint8,)), _ptr(scales, "scales", _BF16_LIKE), epilogue,
+        _ptr(out, "out", _BF16_LIKE), _ptr(topk_ids, "topk_ids", (torch.int32,)),
+        _ptr(topk_weights, "topk_weights", (torch.float32,)), _stream(stream))
+    check(st, "w4a16_moe_gmm_logits")
+
+
 def w4a16_moe_gmm_workspace(x_rows, R, E, K, N):
     return int(lib().w4a16_moe_gmm_workspace(x_rows, R, E, K, N))
 

@@ -114,6 +114,17 @@ def test_streaming_calls_argument_errors():
     assert g(*bad) == w4.W4_ERR_SHAPE
     bad = list(args); bad[12] = w4.W4_OUT_F32
     assert g(*bad) == w4.W4_ERR_ARG
+    gl = lib.w4a16_moe_gmm_logits
+    args = [FAKE, FAKE, 64, 128, 8, 2816, 1408, FAKE, FAKE, w4.W4_EPI_GEGLU_TANH, FAKE, FAKE, FAKE, None]
+    bad = list(args); bad[9] = w4.W4_EPI_NONE       # gated epilogues only
+    assert gl(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[2] = 257
+    assert gl(*bad) == w4.W4_ERR_SHAPE
+    bad = list(args); bad[1] = None
+    assert gl(*bad) == w4.W4_ERR_ARG
+    bad = list(args); bad[6] = 1400                 # N % 32
+    assert gl(*bad) == w4.W4_ERR_SHAPE
+    assert gl(None, None, 0, 128, 8, 2816, 1408, None, None, w4.W4_EPI_GEGLU_TANH, None, None, None, None) == w4.W4_OK
 
 
 def test_route_combine_layer_argument_errors():

@@ -360,3 +360,38 @@ def test_streaming_calls_topk_gmm_ids(T, d, I, E, k):
                                                 oracle.bf16_bits_to_f64(ref["y"]))
     say("  a %.2e/%.2e  o %.2e/%.2e  y %.2e/%.2e" % (a_mx, a_rms, o_mx, o_rms, y_mx, y_rms))
     assert a_ok and o_ok and y_ok
+
+
+@pytest.mark.parametrize("T,d,I,E,k", [(64, 2816, 704, 128, 8), (1, 2816, 704, 128, 8), (40, 1536, 256, 128, 8),
+                                       (64, 256, 96, 16, 4), (100, 2816, 704, 128, 8)])
+def test_gmm_logits_matches_topk_and_gmm_ids(T, d, I, E, k):
+    """w4a16_moe_gmm_logits against w4a16_moe_topk + w4a16_moe_gmm_ids (row_div
+    k) on the same inputs: the ids agree exactly, the weights to fp32
+    rounding (the two sum the softmax in different orders only when one of
+    them is the routing kernel), and the gated outputs bit for bit (the same
+    matmul over the same rows).  The first three shapes rank the logits in
+    the matmul; the others (short K, more than 64 tokens) take the top-k
+    launch."""
+    cfg = dict(id=950, T=T, d=d, I=I, E=E, k=k, router="normal")
+    x, logits, (w1p, w1t, _, _), _ = moe_inputs(cfg, T + d)
+    logits[0, :] = 0.5                                   # ties
+    if T > 3:
+        logits[2, :] = np.round(logits[2, :])
+    say("[gmm logits] T=%d d=%d I=%d E=%d k=%d" % (T, d, I, E, k))
+    dev = "cuda"
+    R = T * k
+    xd, lg, w1q, w1s_d = bf16_dev(x), to_dev(logits), to_dev(w1p), bf16_dev(w1t)
+    ids0 = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts0 = torch.empty(T, k, dtype=torch.float32, device=dev)
+    a0 = torch.full((R, I), float("nan"), dtype=torch.bfloat16, device=dev)
+    w4.w4a16_moe_topk(lg, k, ids0, wts0)
+    w4.w4a16_moe_gmm_ids(xd, ids0, T, k, k, E, d, 2 * I, w1q, w1s_d, w4.W4_EPI_GEGLU_TANH, a0, w4.W4_OUT_BF16)
+    ids1 = torch.full((T, k), -1, dtype=torch.int32, device=dev)
+    wts1 = torch.full((T, k), float("nan"), dtype=torch.float32, device=dev)
+    a1 = torch.full((R, I), float("nan"), dtype=torch.bfloat16, device=dev)
+    w4.w4a16_moe_gmm_logits(xd, lg, k, d, 2 * I, w1q, w1s_d, w4.W4_EPI_GEGLU_TANH, a1, ids1, wts1)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids1.cpu().numpy(), ids0.cpu().numpy())
+    assert np.array_equal(ids1.cpu().numpy(), oracle.moe.route(logits, k)["ids"])
+    assert np.allclose(wts1.cpu().numpy(), wts0.cpu().numpy(), rtol=1e-6, atol=0)
+    assert np.array_equal(bits_host(a1), bits_host(a0))
