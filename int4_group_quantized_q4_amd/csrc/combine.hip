@@ -32,10 +32,11 @@ __device__ __forceinline__ void combine_slots(const void* __restrict__ o, const 
   u32x4 v[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) {
+    // (o is read once: non-temporal loads)
     if constexpr (ODT == W4_OUT_F32)
-      v[c] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(o) + row[c] * N + n0);
+      v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const float*>(o) + row[c] * N + n0));
     else
-      v[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + row[c] * N + n0);
+      v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o) + row[c] * N + n0));
   }
 #pragma unroll
   for (int c = 0; c < NS; ++c) {

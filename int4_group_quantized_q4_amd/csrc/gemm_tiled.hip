@@ -194,6 +194,10 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   __shared__ __align__(16) uint8_t As1[ASTAGE];
   __shared__ __align__(16) uint8_t As2[ASTAGE];
   __shared__ __align__(16) uint8_t As3[ASTAGE];
+  // per row of the block: its activation exponent and its output row, read
+  // at the start so that the epilogue waits for no global load
+  __shared__ int s_xexp[BM];
+  __shared__ int s_orow[BM];
   static_assert(NST == 4, "one array per ring slot");
   auto slot_buf = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
     constexpr int j = decltype(J)::value % NST;
@@ -282,6 +286,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // chunk slot lane%8, which holds source chunk slot ^ aswz(row).
   uint32_t aoff[AQ];   // byte offset of the lane's source chunk in stage 0
   uint32_t ahigh = 0;  // bit q: that chunk lies in the second group of a stage
+  int xe[AQ], orw[AQ];
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
     const int n = AQ * wv + q;
@@ -291,7 +296,23 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
     aoff[q] = (uint32_t)(src * K * 2) + (uint32_t)(ch * 16);
     ahigh |= (ch >= 4 ? 1u : 0u) << q;
+    xe[q] = a.xexp[src];
+    orw[q] = a.out_index ? a.out_index[row] : (int)row;
   }
+  // The first lane of each row's 8 writes the row's entries, once the
+  // pipeline's first loads are issued (so that waiting for xe and orw does not
+  // hold them back); the pipeline's barriers order these writes before the
+  // epilogue's reads.
+  auto stash_rows = [&]() __attribute__((always_inline)) {
+    if ((lane & 7) == 0) {
+#pragma unroll
+      for (int q = 0; q < AQ; ++q) {
+        const int rr = 8 * (AQ * wv + q) + (lane >> 3);
+        s_xexp[rr] = xe[q];
+        s_orow[rr] = orw[q];
+      }
+    }
+  };
   // activations of stage `st` into ring slot J
   auto a_issue = [&](int st, auto J) __attribute__((always_inline)) {
     uint8_t* dst = slot_buf(J) + (AQ * wv) * 1024;
@@ -454,6 +475,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     a_issue(0, std::integral_constant<int, 0>{});
     a_issue(1 <= last_st ? 1 : last_st, std::integral_constant<int, 1>{});
     a_issue(2 <= last_st ? 2 : last_st, std::integral_constant<int, 2>{});
+    stash_rows();
     wait_vm<(NST - 2) * AQ>();
     barrier_only();
 
@@ -486,6 +508,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     if (anybad) return;
   } else {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    stash_rows();
     for (int s = 0; s < S; ++s) {
       __syncthreads();
       a_issue(s, std::integral_constant<int, 0>{});
@@ -532,15 +555,8 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   // D element q of row tile i: row 16i + 4*(lane/16) + q, weight row lane%16 of
   // each tile; the row's activation exponent undoes the fp16 scaling.  bf16
   // results are rounded to nearest even by the hardware conversion.
-  auto row_exp = [&](int rr) __attribute__((always_inline)) {
-    const int64_t row = row_begin + (rr < cnt ? rr : 0);
-    const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
-    return a.xexp[src];
-  };
-  auto dst_row = [&](int rr) __attribute__((always_inline)) -> int64_t {
-    const int64_t row = row_begin + rr;
-    return a.out_index ? (int64_t)a.out_index[row] : row;
-  };
+  auto row_exp = [&](int rr) __attribute__((always_inline)) { return s_xexp[rr]; };
+  auto dst_row = [&](int rr) __attribute__((always_inline)) -> int64_t { return (int64_t)s_orow[rr]; };
   // Gated results go out through LDS (each wave its own 16 KiB ring slot,
   // free once the loop is done): written there in the MFMA layout, read back
   // by rows and stored 16 bytes per lane, so a row's 64-byte segment leaves in
@@ -572,7 +588,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
       const int rr = 16 * k + (lane >> 2);
       if (rr < cnt) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(eb + rr * GS + 16 * (lane & 3));
-        *reinterpret_cast<u32x4*>(obase + dst_row(rr) * (N / 2)) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + dst_row(rr) * (N / 2)));
       }
     }
   } else if constexpr (OUT == W4_OUT_F32) {
@@ -588,7 +604,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         const int ex = row_exp(rr);
         float* orow = static_cast<float*>(a.out) + dst_row(rr) * N + r;
 #pragma unroll
-        for (int t = 0; t < WN_TILES; ++t) orow[tile[t] * kTileRows] = ldexpf(acc[i][t][q], ex);
+        for (int t = 0; t < WN_TILES; ++t) __builtin_nontemporal_store(ldexpf(acc[i][t][q], ex), orow + tile[t] * kTileRows);
       }
     }
   } else {
@@ -603,7 +619,8 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
         uint16_t* orow = static_cast<uint16_t*>(a.out) + dst_row(rr) * N + r;
 #pragma unroll
         for (int t = 0; t < WN_TILES; ++t)
-          orow[tile[t] * kTileRows] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[i][t][q], ex));
+          __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[i][t][q], ex)),
+                                      orow + tile[t] * kTileRows);
       }
     }
   }
