@@ -130,22 +130,27 @@ __device__ __forceinline__ int xcd_item(int b, int total) {
 // Whole-wave; E <= 256.
 struct Item {
   int expert, mtile, nblock;
+  int begin, end;   // the expert's sorted rows [begin, end)
 };
 
 __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blocks, int blk) {
   const int lane = threadIdx.x & 63;
-  int cnt[4], pre = 0;
+  int cnt[4], lo[4], hi[4], pre = 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int e = lane * 4 + s;
-    int n = 0;
+    lo[s] = 0;
+    hi[s] = 0;
     if (offsets) {
-      if (e < E) n = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      if (e < E) {
+        lo[s] = offsets[e];
+        hi[s] = offsets[e + 1];
+      }
     } else if (e == 0) {
-      n = (int)((R + BM - 1) / BM);
+      hi[s] = (int)R;
     }
-    cnt[s] = n;
-    pre += n;
+    cnt[s] = (hi[s] - lo[s] + BM - 1) / BM;
+    pre += cnt[s];
   }
   int incl = pre;
 #pragma unroll
@@ -153,7 +158,7 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
     const int v = __shfl_up(incl, o, 64);
     if (lane >= o) incl += v;
   }
-  Item it{-1, 0, 0};
+  Item it{-1, 0, 0, 0, 0};
   const int total_items = __shfl(incl, 63, 64) * ncol_blocks;
   if (blk >= total_items) return it;
   const int item = xcd_item(blk, total_items);
@@ -161,7 +166,7 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
   const int excl = incl - pre;
   const uint64_t bal = __ballot(lin >= excl && lin < incl);
   const int owner = __ffsll((unsigned long long)bal) - 1;
-  int e = 0, mt = 0;
+  int e = 0, mt = 0, b = 0, en = 0;
   if (lane == owner) {
     int base = excl;
 #pragma unroll
@@ -169,12 +174,16 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
       if (lin >= base && lin < base + cnt[s]) {
         e = lane * 4 + s;
         mt = lin - base;
+        b = lo[s];
+        en = hi[s];
       }
       base += cnt[s];
     }
   }
   it.expert = __shfl(e, owner, 64);
   it.mtile = __shfl(mt, owner, 64);
+  it.begin = __shfl(b, owner, 64);
+  it.end = __shfl(en, owner, 64);
   it.nblock = item - lin * ncol_blocks;
   return it;
 }
@@ -222,8 +231,8 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   const int e = __builtin_amdgcn_readfirstlane(it.expert);
   const int mt = __builtin_amdgcn_readfirstlane(it.mtile);
   const int nb = __builtin_amdgcn_readfirstlane(it.nblock);
-  const int64_t e_begin = a.offsets ? a.offsets[e] : 0;
-  const int64_t e_end = a.offsets ? a.offsets[e + 1] : a.R;
+  const int64_t e_begin = __builtin_amdgcn_readfirstlane(it.begin);
+  const int64_t e_end = __builtin_amdgcn_readfirstlane(it.end);
   const int64_t row_begin = e_begin + (int64_t)mt * BM;
   const int cnt = (int)(e_end - row_begin < BM ? e_end - row_begin : BM);
 
