@@ -10,16 +10,18 @@
 //
 // With K = 704 a 16-row weight tile is 6 KiB: a wave that streams one tile and
 // leaves spends most of its life waiting for its first bytes.  Here a wave
-// takes TPW tiles of its expert (tile i*W + wave of the workgroup's range), with
-// two whole tiles in registers: the next tile's codes and scales are loaded
-// while the current one is multiplied, so only the first tile's latency is
-// exposed.  The expert's activation rows (all of K, at most 16 rows per pass)
-// are staged in LDS once per workgroup, with a table of -136 x each row's sum
-// over each group.  Per group one MFMA takes the bf16 128+u codes with that
-// table entry as its accumulator input, which cancels the +136 bias; the fp32
-// scale per group is applied on the VALU.  A tile's
-// full-block scales (NBF x 128 B, contiguous) are one 128-bit load per lane,
-// parked in a per-wave LDS buffer (one per register set) before use.
+// takes TPW tiles of its expert (tile i*W + wave of the workgroup's range) and
+// streams their blocks one after another (NBF full tile16 blocks per tile,
+// then the partial one) through a ring of 4 blocks in registers, refilled as
+// each block is used, so the weight stream runs on across tile boundaries and
+// only the first block's latency is exposed.  The expert's activation rows
+// (all of K, at most 16 rows per pass) are staged in LDS once per workgroup,
+// with a table of -136 x each row's sum over each group.  Per group one MFMA
+// takes the bf16 128+u codes with that table entry as its accumulator input,
+// which cancels the +136 bias; the fp32 scale per group is applied on the
+// VALU.  A tile's scales (32 G bytes, contiguous) are one 128-bit load per
+// lane issued with the tile's first block and parked in a per-wave LDS buffer
+// when the tile starts.
 
 #include "common.h"
 #include "internal.h"
@@ -29,8 +31,11 @@ namespace w4 {
 
 namespace {
 
-constexpr int kSW = 4;                     // waves per workgroup (each stages the rows once; 3 per CU)
+constexpr int kSW = 4;                     // waves per workgroup (each stages the rows once; 4 per CU)
 constexpr int kTPW = 4;                    // tiles per wave
+constexpr int kRing = 4;                   // code blocks in flight per wave
+constexpr int kWavesPerSimd = 4;
+constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads zeros, moves no bytes
 constexpr int kMaxCols = 1024;             // K limit (8 tile16 blocks)
 constexpr int kRsrcFlags = 0x00020000;     // raw buffer descriptor word 3
 
@@ -47,11 +52,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // IDS: rows from the top-k ids (GemmArgs::ids): activation row r / kslots,
 // output row r.
 template <int NBF, int OUT, bool IDS>
-__global__ void __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(64 * kSW) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) {
-  constexpr int CB = NBF > 0 ? NBF : 1;
+  // A wave's blocks in order: tile i of its kTPW, block b of the tile's NB
+  // (NBF full blocks, then the partial one: gtail groups, or nothing when
+  // gtail = 0).  Codes travel through a ring of D 16-byte registers per lane.
+  constexpr int NB = NBF + 1;
+  constexpr int D = NB < kRing ? NB : kRing;
+  constexpr int STEPS = kTPW * NB;
   __shared__ __align__(16) uint8_t xs[16 * (2 * kMaxCols + 16)];
-  __shared__ __align__(16) uint8_t ssc[kSW * 2 * 1024];
+  __shared__ __align__(16) uint8_t ssc[kSW * 1024];
   __shared__ __align__(16) float ctab[(kMaxCols / kGroup) * 16];   // [G][16]: -136 x group sum of each row
   __shared__ int s_rows[IDS ? kIdsMaxExpertRows : 1];              // the expert's routed rows
   __shared__ int s_wcnt[kSW];                              // per-wave counts of the ids scan
@@ -73,37 +83,40 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
 
-  // tile of iteration i; past the expert's last tile the loads re-read it
-  // and nothing is computed or stored
+  // tile of iteration i; tiles past the expert's last read nothing (offsets
+  // outside the buffers) and are neither computed nor stored
   auto tile_of = [&](int i) { return wgi * kSW * kTPW + i * kSW + wv; };
-  auto load_tile = [&](u32x4* cw, uint32_t* ct, u32x4& sp, uint32_t* st, int i) __attribute__((always_inline)) {
-    int t = tile_of(i);
-    t = t < tiles_per_expert ? t : tiles_per_expert - 1;
-    const uint32_t wt = (uint32_t)t * (uint32_t)(8 * K), stt = (uint32_t)t * (uint32_t)(32 * G);
-#pragma unroll
-    for (int b = 0; b < NBF; ++b)
-      cw[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wt + 1024u * b + 16u * lane, 0, 0));
-    if (NBF > 0)   // lanes past the tile's NBF*128 bytes read the partial block or the next tile: unused
-      sp = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, stt + 16u * lane, 0, 0));
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < gtail) {
-        ct[j] = __builtin_amdgcn_raw_buffer_load_b32(rw, wt + 1024u * NBF + 4u * gtail * lane + 4u * j, 0, 0);
-        st[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, stt + 128u * NBF + 2u * (r * gtail + j), 0, 0);
-      }
+  // codes of step j (tile j / NB, block j % NB) into ring slot j % D, and at
+  // a tile's first block the tile's scales (all its groups: NBF x 128 B, then
+  // the partial block's 16 x gtail; one 16-byte load per lane, lanes past the
+  // tile read the next tile or zeros -- unused) into sp
+  u32x4 cw[D];
+  u32x4 sp = {0u, 0u, 0u, 0u};
+  auto load_step = [&](int j) __attribute__((always_inline)) {
+    const int ti = j / NB, b = j - (j / NB) * NB;   // (j is a compile-time constant here)
+    const int t = tile_of(ti);
+    const bool live = t < tiles_per_expert;
+    const uint32_t wt = (uint32_t)t * (uint32_t)(8 * K);
+    uint32_t off;
+    if (b < NBF) off = wt + 1024u * b + 16u * lane;
+    else off = gtail > 0 ? wt + 1024u * NBF + 4u * gtail * lane : kOOB;
+    cw[j % D] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, live ? off : kOOB, 0, 0));
+    if (b == 0) {
+      const uint32_t so = (uint32_t)t * (uint32_t)(32 * G) + 16u * lane;
+      sp = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, live ? so : kOOB, 0, 0));
+    }
   };
 
-  // The first pass's first tile does not depend on the expert's rows: its
-  // loads go out before the row range is read, so the weight stream starts
-  // without waiting for that read.
-  u32x4 cwA[CB], cwB[CB], spA = {0u, 0u, 0u, 0u}, spB = {0u, 0u, 0u, 0u};
-  uint32_t ctA[3] = {0u, 0u, 0u}, ctB[3] = {0u, 0u, 0u}, stA[3] = {0u, 0u, 0u}, stB[3] = {0u, 0u, 0u};
-  // (the ids go out before the tile: the scan must not wait for the tile to land)
+  // The first pass's ring does not depend on the expert's rows: its loads go
+  // out before the row range is read, so the weight stream starts without
+  // waiting for that read.  (The ids go out before the ring: the scan must not
+  // wait for the ring to land.)
   int idv[8];
   if constexpr (IDS) {
     if (a.R > 512 || wv == 0) ids_batch(a.ids, (int)a.R, wv, idv);
   }
-  load_tile(cwA, ctA, spA, stA, 0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_step(j);
 
   int64_t row_begin = 0, row_end = a.R;
   if constexpr (IDS) {
@@ -133,6 +146,7 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, orange, kRsrcFlags);
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  uint8_t* mys = ssc + wv * 1024;   // this wave's tile scales
 
   for (int64_t row0 = row_begin;;) {
     const int cnt = (int)(row_end - row0 < 16 ? row_end - row0 : 16);
@@ -159,7 +173,7 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
           }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's DMA has landed
+      __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this wave's DMA (and the ring) has landed
       // bias table of the rows this wave staged: -136 x the row's sum over
       // each group, lane g for group g
 #pragma unroll
@@ -187,69 +201,72 @@ short_kernel(GemmArgs a, int wg_per_expert, int total_wg, int tiles_per_expert) 
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       obase[q] = 4 * c + q < cnt ? (uint32_t)((orow(row0 + 4 * c + q) * N + r) * ESZ) : orange;
-    auto run_tile = [&](const u32x4* cw, const uint32_t* ct, const u32x4& sp, const uint32_t* st, int i,
-                        int set) __attribute__((always_inline)) {
-      const int t = tile_of(i);
-      if (t >= tiles_per_expert) return;   // wave-uniform
-      uint8_t* mys = ssc + (wv * 2 + set) * 1024;
-      if (NBF > 0) *reinterpret_cast<u32x4*>(mys + 16 * lane) = sp;
-      f32x4 acc = zero4;
-#pragma unroll
-      for (int b = 0; b < NBF; ++b) {
-        const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + 128 * b + 8 * r);
-        const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16), bf16_to_f32(sv[1] & 0xFFFFu),
-                             bf16_to_f32(sv[1] >> 16)};
-        constexpr int NP = NBF >= 7 ? 1 : 2;   // independent groups at a time (two sets of 7-8 blocks leave room for 1)
-#pragma unroll
-        for (int h = 0; h < 4; h += NP) {
-          bf16x8 A[NP];
-          f32x4 p[NP];
-#pragma unroll
-          for (int j = 0; j < NP; ++j) {
-            A[j] = *reinterpret_cast<const bf16x8*>(xa + (b * 4 + h + j) * 64);
-            p[j] = *reinterpret_cast<const f32x4*>(ca + (b * 4 + h + j) * 64);
-          }
-#pragma unroll
-          for (int j = 0; j < NP; ++j) p[j] = mfma16x16x32(A[j], as_bf16x8(biased_pairs(cw[b][h + j])), p[j]);
-#pragma unroll
-          for (int j = 0; j < NP; ++j) acc += sc[h + j] * p[j];
-        }
-        __builtin_amdgcn_sched_barrier(0);   // one block's operands live at a time
-      }
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < gtail) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (NBF * 4 + j) * 64);
-          const f32x4 cb = *reinterpret_cast<const f32x4*>(ca + (NBF * 4 + j) * 64);
-          const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(ct[j])), cb);
-          acc += bf16_to_f32(st[j]) * p;
-        }
-      // D rows = 4c + q, column = r; rows past the expert's count have an
-      // offset at the end of the output descriptor's range and are dropped
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t off = obase[q] + (uint32_t)(t * kTileRows * ESZ);
-        if constexpr (OUT == W4_OUT_F32)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[q]), ors, off, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(acc[q]), ors, off, 0, 0);
-      }
-    };
 
-    // ping-pong over the two register sets: load tile i+1, multiply tile i
+    f32x4 acc = zero4;
 #pragma unroll
-    for (int i = 0; i < kTPW; i += 2) {
-      if (i + 1 < kTPW) load_tile(cwB, ctB, spB, stB, i + 1);
-      run_tile(cwA, ctA, spA, stA, i, 0);
-      if (i + 1 < kTPW) {
-        if (i + 2 < kTPW) load_tile(cwA, ctA, spA, stA, i + 2);
-        run_tile(cwB, ctB, spB, stB, i + 1, 1);
+    for (int j = 0; j < STEPS; ++j) {
+      const int ti = j / NB, b = j % NB;
+      const int t = tile_of(ti);
+      const bool live = t < tiles_per_expert;   // wave-uniform
+      // a tile's scales to LDS at its first block (this wave's earlier reads
+      // of the buffer complete first: one wave's LDS accesses are in order)
+      if (b == 0) *reinterpret_cast<u32x4*>(mys + 16 * lane) = sp;
+      const u32x4 w = cw[j % D];
+      if (live) {
+        if (b < NBF) {
+          const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + 128 * b + 8 * r);
+          const float sc[4] = {bf16_to_f32(sv[0] & 0xFFFFu), bf16_to_f32(sv[0] >> 16),
+                               bf16_to_f32(sv[1] & 0xFFFFu), bf16_to_f32(sv[1] >> 16)};
+#pragma unroll
+          for (int h = 0; h < 4; h += 2) {
+            bf16x8 A[2];
+            f32x4 p[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              A[jj] = *reinterpret_cast<const bf16x8*>(xa + (b * 4 + h + jj) * 64);
+              p[jj] = *reinterpret_cast<const f32x4*>(ca + (b * 4 + h + jj) * 64);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) p[jj] = mfma16x16x32(A[jj], as_bf16x8(biased_pairs(w[h + jj])), p[jj]);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) acc += sc[h + jj] * p[jj];
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 3; ++g)
+            if (g < gtail) {
+              const bf16x8 A = *reinterpret_cast<const bf16x8*>(xa + (NBF * 4 + g) * 64);
+              const f32x4 cb = *reinterpret_cast<const f32x4*>(ca + (NBF * 4 + g) * 64);
+              const f32x4 p = mfma16x16x32(A, as_bf16x8(biased_pairs(w[g])), cb);
+              const uint32_t sb = *reinterpret_cast<const uint16_t*>(mys + 128 * NBF + 2 * (r * gtail + g));
+              acc += bf16_to_f32(sb) * p;
+            }
+        }
       }
+      // refill the slot: step j + D
+      if (j + D < STEPS) load_step(j + D);
+      if (b == NB - 1) {
+        // D rows = 4c + q, column = r; rows past the expert's count have an
+        // offset at the end of the output descriptor's range and are dropped
+        if (live) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t off = obase[q] + (uint32_t)(t * kTileRows * ESZ);
+            if constexpr (OUT == W4_OUT_F32)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[q]), ors, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(acc[q]), ors, off, 0, 0);
+          }
+        }
+        acc = zero4;
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one block's operands live at a time
     }
     row0 += 16;
     if (row0 >= row_end) break;
     __syncthreads();   // the pass is done with the staged rows
-    load_tile(cwA, ctA, spA, stA, 0);   // the next pass's first tile
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_step(j);   // the next pass's ring
   }
 }
 
