@@ -27,12 +27,11 @@
 //    together with the activation rows (read straight from L2), with no LDS
 //    and no barriers.  The unit's first weight loads go out before its rows
 //    are read.
-//  * fp8_tiled_kernel (many rows per expert, bound by the matrix cores): work
-//    items (expert, 128-row tile, 256-weight-row column block) as in the
-//    W4A16 tiled kernel; 4 waves, each owning 4 weight tiles; per step the
-//    block's activation rows are staged in LDS (padded rows, double
-//    buffered, loaded one step ahead) and the weights come through a
-//    two-step register ring.
+//  * fp8_tiled_kernel (many rows per expert): work items (expert, 128-row
+//    tile, 256-weight-row column block) as in the W4A16 tiled kernel; 4
+//    waves, each owning 4 weight tiles; the block's activation rows go to an
+//    LDS ring of 4 steps by DMA, three steps ahead, and the weights come
+//    through a two-step register ring.
 
 #include <type_traits>
 
@@ -45,6 +44,7 @@ namespace w4 {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNW = 4;                  // waves per block
 constexpr int kWT = 4;                  // 16-row weight tiles per wave
@@ -166,13 +166,63 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol, in
   return it;
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory operations of this
+// wave still in flight, and every LDS access of this wave complete.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence: the waits are explicit.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Chunk swizzle of a staged 128-byte activation row: 16-byte chunk h of row
+// r sits at chunk h ^ aswz(r), which keeps the DMA writes and the operand
+// reads free of bank conflicts.
+__device__ __forceinline__ int aswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Pipeline (one step = 128 bytes of K):
+//  * activations: an LDS ring of 4 steps (16 KiB each, BM = 128 rows), filled
+//    by buffer_load ... lds three steps ahead; one array per ring slot, named
+//    at compile time, so that the compiler's wait before an operand read
+//    covers only that slot's DMA;
+//  * weights: each lane's 32 bytes of its 4 tiles' rows per step, a register
+//    ring D = 2 steps deep;
+//  * every step issues the same number of loads (re-reads past the end), so
+//    the wait at a step's end is a constant: A(s+1) has landed once at most
+//    32 loads are younger (B(s), A(s+2), B(s+1), A(s+3), B(s+2)); the
+//    prologue issues A(0), A(1), B(0), A(2), B(1), which makes that count
+//    hold from the first step on.
 template <int MT, int D, int EPI, int OUT>
 __global__ void __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2)))
 fp8_tiled_kernel(Fp8Args a, int ncol) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   constexpr int BM = 16 * MT;
-  constexpr int ABUF = BM * kAStride;
-  __shared__ __align__(16) uint8_t As[2 * ABUF];
+  constexpr int NST = 4;
+  constexpr int ASTAGE = BM * kKS;                   // 16 KiB
+  constexpr int AQ = ASTAGE / (1024 * kNW);          // DMA instructions per wave per step
+  static_assert(D == 2, "the end-of-step wait assumes a two-step weight ring");
+  __shared__ __align__(16) uint8_t As0[ASTAGE];
+  __shared__ __align__(16) uint8_t As1[ASTAGE];
+  __shared__ __align__(16) uint8_t As2[ASTAGE];
+  __shared__ __align__(16) uint8_t As3[ASTAGE];
+  auto slot_buf = [&](auto J) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int j = decltype(J)::value % NST;
+    if constexpr (j == 0) return As0;
+    else if constexpr (j == 1) return As1;
+    else if constexpr (j == 2) return As2;
+    else return As3;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,7 +241,8 @@ fp8_tiled_kernel(Fp8Args a, int ncol) {
   const int cnt = (int)(e_end - row_begin < BM ? e_end - row_begin : BM);
 
   // this wave's weight tiles; in a last, partial column block the waves
-  // without tiles stage activations and meet the barriers only
+  // without tiles stage activations and meet the barriers only (their
+  // weight loads read nothing, so every wave's load count is the same)
   const int tiles_total = (int)(N / kTileRows);
   int tile[kWT];
   bool active;
@@ -218,6 +269,7 @@ fp8_tiled_kernel(Fp8Args a, int ncol) {
   }
 
   const int nks = (int)((K + kKS - 1) / kKS);
+  const int last = nks - 1;
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.wq + (int64_t)e * N * K), 0, (int)(N * K), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rx =
@@ -227,47 +279,46 @@ fp8_tiled_kernel(Fp8Args a, int ncol) {
   uint32_t woff[kWT];
 #pragma unroll
   for (int t = 0; t < kWT; ++t) woff[t] = (uint32_t)((int64_t)(tile[t] * kTileRows + r) * K) + 32u * (uint32_t)c;
-  u32x4 bw[D][kWT][2];
+  i32x8 bw[D][kWT];
+  // (offsets of dead lanes get bit 31 set -- past every range, so they read
+  // zeros -- by arithmetic, not a select the compiler could turn into
+  // branches around the loads)
   auto b_issue = [&](int slot, int ks) __attribute__((always_inline)) {
-    if (!active) return;   // wave-uniform
-    const bool live = (int64_t)ks * kKS + 32 * c < K;
+    const uint32_t dead = (uint32_t)(!active || (int64_t)ks * kKS + 32 * c >= K);
 #pragma unroll
     for (int t = 0; t < kWT; ++t) {
-      const uint32_t off = live ? woff[t] + (uint32_t)(ks * kKS) : kOOB;
-      bw[slot][t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
-      bw[slot][t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16u, 0, 0));
+      const uint32_t off = (woff[t] + (uint32_t)(ks * kKS)) | (dead << 31);
+      const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+      const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16u, 0, 0));
+      bw[slot][t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
-  // activation staging: the block's BM rows x 128 bytes per step, 16-byte
-  // chunks; thread p stages chunk p % 8 of row p / 8 (+ 256 per round)
-  constexpr int NCH = BM * 8;                             // chunks per step
-  constexpr int NAQ = (NCH + 64 * kNW - 1) / (64 * kNW);  // chunks per thread
-  uint32_t aoff[NAQ];
-  int adst[NAQ];
+  // activation DMA: wave wv's instruction q fills bytes [1024n, 1024n + 1024)
+  // of a step buffer, n = AQ*wv + q: rows 8n .. 8n+7, lane -> row 8n + lane/8,
+  // chunk slot lane % 8, which holds source chunk slot ^ aswz(row); chunks
+  // past K read zeros
+  uint32_t aoff[AQ];
+  int achk[AQ];
 #pragma unroll
-  for (int q = 0; q < NAQ; ++q) {
-    const int p = (int)threadIdx.x + q * 64 * kNW;
-    const int rr = p >> 3, ch = p & 7;
+  for (int q = 0; q < AQ; ++q) {
+    const int n = AQ * wv + q;
+    const int rr = 8 * n + (lane >> 3);
+    const int ch = (lane & 7) ^ aswz(rr);
     const int64_t row = row_begin + (rr < cnt ? rr : 0);
     const int64_t src = a.row_index ? (int64_t)a.row_index[row] : row;
-    aoff[q] = (p < NCH) ? (uint32_t)(src * K) + 16u * (uint32_t)ch : kOOB;
-    adst[q] = rr * kAStride + ch * 16;
+    aoff[q] = (uint32_t)(src * K) + 16u * (uint32_t)ch;
+    achk[q] = 16 * ch;
   }
-  u32x4 ar[NAQ];
-  auto a_load = [&](int ks) __attribute__((always_inline)) {
+  auto a_issue = [&](int st, auto J) __attribute__((always_inline)) {
+    uint8_t* dst = slot_buf(J) + (AQ * wv) * 1024;
 #pragma unroll
-    for (int q = 0; q < NAQ; ++q) {
-      const int ch = ((int)threadIdx.x + q * 64 * kNW) & 7;
-      const bool live = aoff[q] != kOOB && (int64_t)ks * kKS + 16 * ch < K;
-      const uint32_t off = live ? aoff[q] + (uint32_t)(ks * kKS) : kOOB;
-      ar[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    for (int q = 0; q < AQ; ++q) {
+      const uint32_t dead = (uint32_t)((int64_t)st * kKS + achk[q] >= K);
+      const uint32_t voff = (aoff[q] + (uint32_t)(st * kKS)) | (dead << 31);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16,
+                                               voff, 0, 0, 0);
     }
-  };
-  auto a_store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < NAQ; ++q)
-      if ((int)threadIdx.x + q * 64 * kNW < NCH) *reinterpret_cast<u32x4*>(As + buf * ABUF + adst[q]) = ar[q];
   };
 
   f32x4 acc[MT][kWT];
@@ -276,53 +327,61 @@ fp8_tiled_kernel(Fp8Args a, int ncol) {
 #pragma unroll
     for (int t = 0; t < kWT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: the ring's first D steps of weights, step 0's activations
-#pragma unroll
-  for (int s = 0; s < D; ++s) b_issue(s, s < nks ? s : nks - 1);
-  a_load(0);
-  a_store(0);
-  __syncthreads();
+  // operand reads: row 16i + r, K bytes 32c .. 32c+31 = chunks 2c, 2c+1
+  const int apos_lo = r * kKS + ((2 * c) ^ aswz(r)) * 16;
+  const int apos_hi = r * kKS + ((2 * c + 1) ^ aswz(r)) * 16;
+  auto read_a = [&](const uint8_t* Ab, int i) __attribute__((always_inline)) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(Ab + apos_lo + i * 16 * kKS);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(Ab + apos_hi + i * 16 * kKS);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
-  const int apos = r * kAStride + 32 * c;
-  auto step = [&](int ks, auto SLOT) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SLOT)::value;
-    const int buf = ks & 1;
-    if (ks + 1 < nks) a_load(ks + 1);
+  auto step = [&](int s, auto J) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;   // s % NST
+    constexpr int sl = j % D;               // s % D
+    a_issue(s + NST - 1 <= last ? s + NST - 1 : last, IC<j + NST - 1>{});
+    __builtin_amdgcn_sched_barrier(0);
     if (active) {
-      i32x8 B[kWT];
-#pragma unroll
-      for (int t = 0; t < kWT; ++t) {
-        const u32x4 lo = bw[sl][t][0], hi = bw[sl][t][1];
-        B[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
+      const uint8_t* Ab = slot_buf(J);
+      i32x8 A = read_a(Ab, 0);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint8_t* ap = As + buf * ABUF + apos + i * 16 * kAStride;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(ap);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(ap + 16);
-        const i32x8 A = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const i32x8 An = i + 1 < MT ? read_a(Ab, i + 1) : A;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < kWT; ++t) acc[i][t] = mfma_fp8(A, B[t], acc[i][t]);
+        for (int t = 0; t < kWT; ++t) acc[i][t] = mfma_fp8(A, bw[sl][t], acc[i][t]);
+        __builtin_amdgcn_sched_barrier(0);
+        A = An;
       }
     }
-    // refill the slot with step ks + D (clamped: the loads in flight stay
-    // the same in number at every step)
-    const int kn = ks + D < nks ? ks + D : nks - 1;
-    b_issue(sl, kn);
-    if (ks + 1 < nks) a_store(buf ^ 1);
-    __syncthreads();
+    b_issue(sl, s + D <= last ? s + D : last);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<3 * 2 * kWT + 2 * AQ>();   // A(s+1) has landed (see above)
+    barrier_only();
   };
-  int ks = 0;
+
+  // prologue, in the order the steps would have issued them: A(0), A(1),
+  // B(0), A(2), B(1); then wait for A(0)
+  a_issue(0, IC<0>{});
+  a_issue(1 <= last ? 1 : last, IC<1>{});
+  b_issue(0, 0);
+  a_issue(2 <= last ? 2 : last, IC<2>{});
+  b_issue(1, 1 <= last ? 1 : last);
+  wait_vm<2 * 2 * kWT + 2 * AQ>();
+  barrier_only();
+
+  int s = 0;
 #pragma unroll 1
-  for (; ks + D <= nks; ks += D) {
-    [&]<int... S>(std::integer_sequence<int, S...>) {
-      (step(ks + S, std::integral_constant<int, S>{}), ...);
-    }(std::make_integer_sequence<int, D>{});
+  for (; s + 3 < nks; s += 4) {
+    step(s, IC<0>{});
+    step(s + 1, IC<1>{});
+    step(s + 2, IC<2>{});
+    step(s + 3, IC<3>{});
   }
-  [&]<int... S>(std::integer_sequence<int, S...>) {
-    ((ks + S < nks ? step(ks + S, std::integral_constant<int, S>{}) : void()), ...);
-  }(std::make_integer_sequence<int, D>{});
-  __builtin_amdgcn_s_waitcnt(0);   // the clamped refills past the end
+  if (s < nks) step(s, IC<0>{});
+  if (s + 1 < nks) step(s + 1, IC<1>{});
+  if (s + 2 < nks) step(s + 2, IC<2>{});
+  wait_vm<0>();   // the re-reads past the end
 
   if (!active) return;
   // D element q of row tile i: row 16i + 4c + q, weight row r of each tile
