@@ -32,7 +32,7 @@ namespace w4 {
 namespace {
 
 constexpr int kSW = 4;                     // waves per workgroup (each stages the rows once; 4 per CU)
-constexpr int kTPW = 4;                    // tiles per wave
+constexpr int kTPW = 6;                    // tiles per wave
 constexpr int kRing = 4;                   // code blocks in flight per wave
 constexpr int kWavesPerSimd = 4;
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads zeros, moves no bytes
