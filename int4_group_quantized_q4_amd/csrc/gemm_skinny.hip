@@ -27,6 +27,8 @@
 // Rows beyond the expert's count read a valid row; their results are never
 // stored.
 
+#include <cmath>
+
 #include "common.h"
 #include "internal.h"
 #include "w4a16.h"
@@ -131,7 +133,8 @@ __device__ __forceinline__ int expert_rows_from_logits(const float lg[kLogitsPer
 // entries of the top-k plan (ids_out, wts_out) between them.
 template <int MAXT, int EPI, int OUT, int D, int RM>
 __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmArgs a, int wg_per_expert,
-                                                                           int total_wg, int units_per_expert) {
+                                                                           int total_wg, int units_per_expert,
+                                                                           int tsets) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   constexpr bool IDS = RM != 0;
   constexpr int CB = D > 4 ? D : 4;       // blocks per staged activation chunk
@@ -161,26 +164,36 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   const int c = lane >> 4;
   const int64_t K = a.K, N = a.N;
 
-  // this wave's weight tile
-  int unit, tile;
-  if constexpr (GATED) {
-    unit = wgi * (kWaves / 2) + (wv >> 1);           // gate/up pair
-    tile = unit + ((wv & 1) ? (int)(N / 32) : 0);    // the up tile sits N/2 rows below
-  } else {
-    unit = wgi * kWaves + wv;
-    tile = unit;
-  }
-  // idle waves (past the expert's last tile) run on tile 0 and store nothing,
-  // so every wave executes the same loads and barriers
-  const bool active = unit < units_per_expert;
-  if (!active) tile = 0;
-
   const int G = (int)(K / kGroup);
   const int NBF = G / kBlockGroups;
   const int gtail = G - NBF * kBlockGroups;
   const int NBall = NBF + (gtail > 0 ? 1 : 0);
-  const uint8_t* wb = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)tile * 8 * K;
-  const uint16_t* sb = a.scales + ((int64_t)e * N + (int64_t)tile * kTileRows) * G;
+
+  // The workgroup takes tsets sets of units one after another (tsets > 1
+  // when the expert's units would otherwise need more than one round of
+  // resident workgroups); this wave's weight tile in set ts.  Idle waves
+  // (past the expert's last tile) run on tile 0 and store nothing, so every
+  // wave executes the same loads and barriers.
+  constexpr int PER_WG = GATED ? kWaves / 2 : kWaves;
+  int unit, tile;
+  bool active;
+  const uint8_t* wb;
+  const uint16_t* sb;
+  auto set_tiles = [&](int ts) __attribute__((always_inline)) {
+    const int u0 = (wgi * tsets + ts) * PER_WG;
+    if constexpr (GATED) {
+      unit = u0 + (wv >> 1);                           // gate/up pair
+      tile = unit + ((wv & 1) ? (int)(N / 32) : 0);    // the up tile sits N/2 rows below
+    } else {
+      unit = u0 + wv;
+      tile = unit;
+    }
+    active = unit < units_per_expert;
+    if (!active) tile = 0;
+    wb = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)tile * 8 * K;
+    sb = a.scales + ((int64_t)e * N + (int64_t)tile * kTileRows) * G;
+  };
+  set_tiles(0);
 
   u32x4 cw[D];
   auto load_block = [&](int slot, int b) __attribute__((always_inline)) {
@@ -245,7 +258,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   const int NSP = (NBF + SPB - 1) / SPB;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
-  const uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
+  uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
   auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i)
@@ -257,7 +270,18 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     for (int i = 0; i < SPL; ++i) *reinterpret_cast<u32x4*>(mys + 1024 * i + 16 * lane) = t[i];
   };
 
-  // the partial last block (1..3 groups), loaded once
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int ts = 0; ts < tsets; ++ts) {
+  if (ts > 0) {
+    set_tiles(ts);
+    // a set with no unit of the expert (the expert's last workgroup) ends the
+    // workgroup's work: units grow with the wave index, so wave 0 decides
+    const int u0 = (wgi * tsets + ts) * PER_WG;
+    if (u0 >= units_per_expert) break;   // uniform over the workgroup
+    sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
+  }
+  // the partial last block (1..3 groups), loaded once per set
   uint32_t ct[3] = {0u, 0u, 0u};
   float st[3] = {0.f, 0.f, 0.f};
   if (gtail > 0) {
@@ -268,8 +292,6 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
         st[j] = bf16_to_f32(sb[64 * (int64_t)NBF + r * gtail + j]);
       }
   }
-
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // Activation staging: chunk ch (columns [ch*KC, ch*KC+KC)) of the pass's rows
   // goes to LDS buffer ch%2.  The global loads of chunk ch+1 are issued before
@@ -353,7 +375,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     if (NBF > 0) {
       u32x4 s0[SPL];
       span_load(s0, 0);
-      if (row0 != row_begin) {   // (the first pass's ring is already in flight)
+      if (ts > 0 || row0 != row_begin) {   // (the first pass's ring is already in flight)
 #pragma unroll
         for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
       }
@@ -500,6 +522,42 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       }
     }
   }
+  }   // tile sets
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Workgroups per expert and unit sets per workgroup: one set is PER_WG units
+// (tiles, or gate/up pairs); a workgroup takes several sets one after another
+// when the experts' sets would not fit in one round of resident workgroups
+// (wg_per_cu of them per CU), so the launch runs as one round.  Only where
+// that pays: the experts that get rows (expected E (1 - (1 - 1/E)^R) of them
+// for R routed rows) must fill at least two rounds of one-set workgroups (at
+// 8 tokens, 0.6 rounds' worth, three sets per workgroup took 67.6 against
+// 57.1 us per layer), and at most 4 rows per expert on average: with more,
+// the experts' row counts differ enough (some take a second 16-row pass)
+// that the dispatcher's balancing over several rounds does better (128
+// tokens: 103.4 against 108.6 us per layer; 256 tokens: 151 against 160 us).
+void decode_grid(const GemmArgs& a, int units, int per_wg, int wg_per_cu, int* wg_per_expert, int* tsets) {
+  const int sets = (units + per_wg - 1) / per_wg;
+  const double slots = (double)wg_per_cu * device_cus();
+  const double touched = a.E * (1.0 - std::pow(1.0 - 1.0 / a.E, (double)a.R));
+  int ts = (int)std::ceil(sets * touched / slots);
+  if (sets * touched < 2.0 * slots || a.R > 4 * (int64_t)a.E) ts = 1;
+  ts = ts < 1 ? 1 : (ts > sets ? sets : ts);
+  *tsets = ts;
+  *wg_per_expert = (sets + ts - 1) / ts;
 }
 
 template <int MAXT, int D, int IDS>
@@ -507,21 +565,25 @@ void launch_m_ids(const GemmArgs& a, hipStream_t stream) {
   const bool gated = a.epilogue != W4_EPI_NONE;
   const int units = (int)(gated ? a.N / 32 : a.N / 16);
   const int per_wg = gated ? kWaves / 2 : kWaves;
-  const int wg_per_expert = (units + per_wg - 1) / per_wg;
+  // resident 8-wave workgroups per CU: two at 4 waves per SIMD (the one-tile
+  // kernel with the 4-block ring), one otherwise
+  const int wg_per_cu = (MAXT == 1 && D == kDecodeRing) ? 2 : 1;
+  int wg_per_expert, tsets;
+  decode_grid(a, units, per_wg, wg_per_cu, &wg_per_expert, &tsets);
   const int total = wg_per_expert * a.E;
   dim3 grid(total), block(64 * kWaves);
   if (a.epilogue == W4_EPI_GEGLU_TANH)
     hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_GEGLU_TANH, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
-                       wg_per_expert, total, units);
+                       wg_per_expert, total, units, tsets);
   else if (a.epilogue == W4_EPI_SWIGLU)
     hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_SWIGLU, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
-                       wg_per_expert, total, units);
+                       wg_per_expert, total, units, tsets);
   else if (a.out_dtype == W4_OUT_F32)
     hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_F32, D, IDS>), grid, block, 0, stream, a,
-                       wg_per_expert, total, units);
+                       wg_per_expert, total, units, tsets);
   else
     hipLaunchKernelGGL((decode_kernel<MAXT, W4_EPI_NONE, W4_OUT_BF16, D, IDS>), grid, block, 0, stream, a,
-                       wg_per_expert, total, units);
+                       wg_per_expert, total, units, tsets);
 }
 
 template <int MAXT, int D>
@@ -530,14 +592,15 @@ void launch_m(const GemmArgs& a, hipStream_t stream) {
     if (a.logits) {
       // (gated only: gemm_skinny_takes_logits)
       const int units = (int)(a.N / 32);
-      const int wg_per_expert = (units + kWaves / 2 - 1) / (kWaves / 2);
+      int wg_per_expert, tsets;
+      decode_grid(a, units, kWaves / 2, 2, &wg_per_expert, &tsets);
       const int total = wg_per_expert * a.E;
       if (a.epilogue == W4_EPI_GEGLU_TANH)
         hipLaunchKernelGGL((decode_kernel<1, W4_EPI_GEGLU_TANH, W4_OUT_BF16, kDecodeRing, 2>), dim3(total),
-                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units);
+                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units, tsets);
       else
         hipLaunchKernelGGL((decode_kernel<1, W4_EPI_SWIGLU, W4_OUT_BF16, kDecodeRing, 2>), dim3(total),
-                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units);
+                           dim3(64 * kWaves), 0, stream, a, wg_per_expert, total, units, tsets);
       return;
     }
   }
