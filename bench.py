@@ -256,26 +256,33 @@ def warm_up(step, warmup):
     return n
 
 
+# every EVENT_STRIDE-th layer of the timed region carries the two events
+# around its gate/up GEMM (each record adds about a microsecond of stream
+# time, which the other layers are spared)
+EVENT_STRIDE = 4
+
+
 def time_moe(cfg, steps, warmup, copies=3, seed=1234):
-    """Timed region: `steps` layers with HIP events around the gate/up GEMM
-    only (its average launch time, and the whole-layer time).  Afterwards, an
-    instrumented pass with events between all four calls gives the per-call
-    breakdown (route, gate/up, down, combine), whose event records add a few
-    microseconds to each call."""
+    """Timed region: `steps` layers, every EVENT_STRIDE-th with HIP events
+    around its gate/up GEMM (that GEMM's average launch time), and the
+    whole-layer time.  Afterwards, an instrumented pass with events between
+    all four calls gives the per-call breakdown (route, gate/up, down,
+    combine), whose event records add a few microseconds to each call."""
     dev = torch.device("cuda:0")
     ls = MoeLayerSet(cfg, copies, seed, dev)
     touched = [ls.touched(c)[0] for c in range(copies)]
     warm_up(lambda i: ls.step(i % copies), warmup)
-    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
+    timed = list(range(0, steps, EVENT_STRIDE))
+    evs = {i: [TimingEvent() for _ in range(2)] for i in timed}
     torch.cuda.synchronize()
     start, stop = TimingEvent(), TimingEvent()
     start.record()
     for i in range(steps):
-        ls.step(i % copies, evs[i])
+        ls.step(i % copies, evs.get(i))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    g1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    g1 = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
     nb = min(steps, 30)
     evb = [[TimingEvent() for _ in range(5)] for _ in range(nb)]
     for i in range(nb):
