@@ -840,7 +840,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip dense decode, e2e and the ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU only (--gpus must be 1): there is no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
