@@ -196,9 +196,10 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
  * One (expert's) weight matrix must stay below 2 GiB of codes (N*K/2 < 2^31),
  * else W4_ERR_SHAPE.
  *   split-K kernel    (w4a16_linear with M <= 16 and fewer than 4096 16-row
- *                     tiles) the streaming kernel's products, per 1024-column
- *                     slice of K; the slices' fp32 partial sums go to the
- *                     workspace and are added in slice order.
+ *                     tiles) the streaming kernel's products, per slice of K
+ *                     (1024 columns; 512 at K <= 4096 with M = 1); the
+ *                     slices' fp32 partial sums are added in slice order, in
+ *                     LDS at K <= 4096, else through the workspace.
  * The tiled kernel needs a workspace for the fp16 activation rows, the split-K
  * kernel one for its partial sums: w4a16_linear_workspace /
  * w4a16_moe_gmm_workspace bytes, 16-byte aligned.  A call that selects the

@@ -465,7 +465,11 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
           if (j < gtail) {
-            const bf16x8 B = as_bf16x8(biased_pairs(ct[j]));
+            // converted here: hoisted out of the pass loop, the pairs would
+            // hold 12 registers through the main loop
+            uint32_t w = ct[j];
+            asm volatile("" : "+v"(w));
+            const bf16x8 B = as_bf16x8(biased_pairs(w));
 #pragma unroll
             for (int tt = 0; tt < MAXT; ++tt)
               if (tt < ntt) {

@@ -22,12 +22,14 @@
 // slices and rounds.
 //
 // For K <= 4096 (every activation row of the call fits in LDS) one kernel
-// does it all: a workgroup of 16 waves holds 4 weight tiles x 4 K-slices, the
-// activation rows are staged in LDS once, and after the slices' MFMAs the
-// partial sums meet in LDS and are added in slice order (the order of the
-// two-kernel path, so the results are the same bits) and rounded by the
-// slice-0 waves.  No workspace, no second launch, no ordering between
-// workgroups.
+// does it all: a workgroup holds FT weight tiles x FS K-slices, one wave
+// each (4 x 4 for up to 16 rows, 2 x 4 for up to 8 or 4, 1 x 8 for one row),
+// the activation rows are staged in LDS once, and after the slices' MFMAs the
+// partial sums meet in LDS and are added in slice order and rounded by the
+// slice-0 waves.  With 4 slices at K = 4096 each slice is 1024 columns, the
+// slicing of the two-kernel path, so both give the same bits; one row is
+// summed over 8 slices of 512 columns.  No workspace, no second launch, no
+// ordering between workgroups.
 
 #include "common.h"
 #include "internal.h"
@@ -160,17 +162,18 @@ __global__ void __launch_bounds__(64 * kSKWaves) splitk_partial_kernel(GemmArgs 
   }
 }
 
-constexpr int kFTiles = 4;                          // weight tiles per fused workgroup
-constexpr int kFSlices = 4;                         // K-slices per fused workgroup
 constexpr int kFMaxK = 4096;
 constexpr int kFXStride = kFMaxK * 2 + 16;          // LDS row stride of the staged activations
-constexpr int kFMaxBlocks = 8;                      // tile16 blocks per slice at K = 4096
 
-// grid: tile groups of kFTiles; wave wv: tile wv % 4, slice wv / 4; each slice
-// spans sb blocks (the partial block counts as one).
-template <int OUT>
-__global__ void __launch_bounds__(64 * kFTiles * kFSlices) splitk_fused_kernel(GemmArgs a, int sb) {
-  __shared__ __align__(16) uint8_t xs[kMaxRows * kFXStride];
+// MR: activation rows staged (the call's M <= MR); FT weight tiles x FS
+// K-slices per workgroup, one wave each.  grid: tile groups of FT; wave wv:
+// tile wv % FT, slice wv / FT; each slice spans sb blocks (the partial block
+// counts as one), at most kFMaxK / 128 / FS.
+template <int OUT, int MR, int FT, int FS>
+__global__ void __launch_bounds__(64 * FT * FS) splitk_fused_kernel(GemmArgs a, int sb) {
+  constexpr int kFTiles = FT, kFSlices = FS;
+  constexpr int kFMaxBlocks = (kFMaxK / 128 + FS - 1) / FS;   // tile16 blocks per slice, at most
+  __shared__ __align__(16) uint8_t xs[MR * kFXStride];
   __shared__ __align__(16) uint8_t ssc[kFTiles * kFSlices * 1024];   // scale spans, then the partial sums
 
   const int lane = threadIdx.x & 63;
@@ -205,7 +208,8 @@ __global__ void __launch_bounds__(64 * kFTiles * kFSlices) splitk_fused_kernel(G
   // only, so the blocks are still arriving when the MFMAs start.  Loads that
   // are not needed get an offset past their descriptor's range and return
   // zeros.
-  constexpr int kXP = kMaxRows * (kFMaxK / 8) / (64 * kFTiles * kFSlices);   // pieces per thread, at most
+  constexpr int kXP = MR * (kFMaxK / 8) / (64 * kFTiles * kFSlices);   // pieces per thread, at most
+  static_assert(kXP * 64 * kFTiles * kFSlices == MR * (kFMaxK / 8), "the rows split evenly over the threads");
   constexpr uint32_t kOff = 0x80000000u;                                     // past every range
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, (int)(M * K * 2), kRsrcFlags);
   u32x4 xv[kXP];
@@ -334,23 +338,36 @@ static bool fused_fits(const GemmArgs& a);
 bool gemm_splitk_needs_workspace(const GemmArgs& a) { return !fused_fits(a); }
 
 static bool fused_fits(const GemmArgs& a) {
+  // the fused kernel reads the activation rows as one contiguous block; any
+  // K <= kFMaxK fits its slices
+  return !a.row_index && a.K <= kFMaxK;
+}
+
+template <int MR, int FT, int FS>
+void launch_fused(const GemmArgs& a, hipStream_t stream) {
   const int64_t G = a.K / kGroup;
-  const int64_t nball = (G + kBlockGroups - 1) / kBlockGroups;
-  // the fused kernel reads the activation rows as one contiguous block
-  return !a.row_index && a.K <= kFMaxK && (nball + kFSlices - 1) / kFSlices <= kFMaxBlocks;
+  const int nball = (int)((G + kBlockGroups - 1) / kBlockGroups);
+  const int sb = (nball + FS - 1) / FS;
+  const int groups = (int)((a.N / kTileRows + FT - 1) / FT);
+  const dim3 grid((unsigned)groups), block(64 * FT * FS);
+  if (a.out_dtype == W4_OUT_F32)
+    hipLaunchKernelGGL((splitk_fused_kernel<W4_OUT_F32, MR, FT, FS>), grid, block, 0, stream, a, sb);
+  else
+    hipLaunchKernelGGL((splitk_fused_kernel<W4_OUT_BF16, MR, FT, FS>), grid, block, 0, stream, a, sb);
 }
 
 void launch_gemm_splitk(const GemmArgs& a, void* ws, hipStream_t stream) {
   if (fused_fits(a)) {
-    const int64_t G = a.K / kGroup;
-    const int nball = (int)((G + kBlockGroups - 1) / kBlockGroups);
-    const int sb = (nball + kFSlices - 1) / kFSlices;
-    const int groups = (int)((a.N / kTileRows + kFTiles - 1) / kFTiles);
-    const dim3 grid((unsigned)groups), block(64 * kFTiles * kFSlices);
-    if (a.out_dtype == W4_OUT_F32)
-      hipLaunchKernelGGL(splitk_fused_kernel<W4_OUT_F32>, grid, block, 0, stream, a, sb);
-    else
-      hipLaunchKernelGGL(splitk_fused_kernel<W4_OUT_BF16>, grid, block, 0, stream, a, sb);
+    // LDS holds the rows the call has (1, 4, 8 or 16 of them), so that more
+    // workgroups are resident at once; the activations of one row take so
+    // little that 1 tile x 8 slices per workgroup fit (a 14336-row matrix:
+    // 7168 waves of 4 blocks each).  At K = 4096, N = 14336 (16 rotating
+    // weight copies) against 4 x 4 tiles x slices with 16 rows staged for
+    // every M: M = 1 12.1 -> 9.5 us, M = 8 12.4 -> 11.8 us.
+    if (a.R == 1) launch_fused<1, 1, 8>(a, stream);
+    else if (a.R <= 4) launch_fused<4, 2, 4>(a, stream);
+    else if (a.R <= 8) launch_fused<8, 2, 4>(a, stream);
+    else launch_fused<kMaxRows, 4, 4>(a, stream);
     return;
   }
   const int ns = slices_of(a.K);
