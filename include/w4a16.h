@@ -191,8 +191,8 @@ int q4_pack_scales(const uint16_t* scales, int64_t rows, int64_t K, uint16_t* sc
  *                     per-row power of two (exact for every value within 2^32
  *                     of the row's largest magnitude; smaller ones round to
  *                     fp16's finest step).  A block meeting a scale outside that
- *                     range is recomputed by a second kernel with per-group
- *                     fp32 scaling.
+ *                     range recomputes its tile, in the same launch, with
+ *                     per-group fp32 scaling.
  * One (expert's) weight matrix must stay below 2 GiB of codes (N*K/2 < 2^31),
  * else W4_ERR_SHAPE.
  *   split-K kernel    (w4a16_linear with M <= 16 and fewer than 4096 16-row

@@ -188,13 +188,13 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
   return it;
 }
 
-// EXACT = false: the fast path; a block that meets a scale outside the exact
-// fp16 range stores nothing and sets redo[block].  EXACT = true (launched
-// next, same grid): only blocks with redo set run, recomputing their tile with
-// B = q in fp16 and each group's fp32 partial sum times its fp32 scale.
-template <int EPI, int OUT, bool EXACT>
+// The fast path computes the block's tile with B = s*q in fp16.  A block that
+// meets a scale outside the exact fp16 range anywhere in its tile then
+// recomputes the tile in place with B = q in fp16 and each group's fp32
+// partial sum times its fp32 scale (the exact path), before the epilogue.
+template <int EPI, int OUT>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2)))
-tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
+tiled_kernel(GemmArgs a, int ncol_blocks) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   // One array per ring slot, every access naming its slot at compile time: the
   // compiler then tells the slots apart and waits, before an operand read, only
@@ -222,10 +222,6 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
   const int c = lane >> 4;
   const int64_t K = a.K, N = a.N;
 
-  // (redo[] is valid only for blocks that hold an item; find_item decides)
-  if constexpr (EXACT) {
-    if (redo[blockIdx.x] == 0) return;
-  }
   const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, blockIdx.x);
   if (it.expert < 0) return;   // uniform over the block
   const int e = __builtin_amdgcn_readfirstlane(it.expert);
@@ -478,7 +474,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     barrier_only();
   };
 
-  if constexpr (!EXACT) {
+  {
     // prologue: block 0, then A(0) .. A(NST-2); wait for A(0) and block 0
     bblk_issue(0, std::integral_constant<int, 0>{});
     a_issue(0, std::integral_constant<int, 0>{});
@@ -509,15 +505,18 @@ tiled_kernel(GemmArgs a, int ncol_blocks, uint8_t* redo) {
     // block's LDS is released
     wait_vm<0>();
 
-    // Any scale outside the exact fp16 range anywhere in the block: leave the
-    // block to the exact kernel.
-    const bool bad = srange[0] >= kScaleSpan || srange[1] >= kScaleSpan;
-    const int anybad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) redo[blockIdx.x] = anybad ? 1 : 0;
-    if (anybad) return;
-  } else {
+  }
+  // Any scale outside the exact fp16 range anywhere in the block: the fast
+  // path's sums are discarded and the exact path recomputes the tile.  (The
+  // row entries stashed in the prologue stay valid; the barrier inside
+  // __syncthreads_or comes after every wave's last read of the ring.)
+  const bool bad = srange[0] >= kScaleSpan || srange[1] >= kScaleSpan;
+  if (__syncthreads_or(bad)) {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    stash_rows();
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < WN_TILES; ++t) acc[i][t] = zero4;
     for (int s = 0; s < S; ++s) {
       __syncthreads();
       a_issue(s, std::integral_constant<int, 0>{});
@@ -697,22 +696,17 @@ static int64_t tiled_grid(const GemmArgs& a, int* ncol_blocks) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// fp16 activation rows and their exponents
 size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int64_t N) {
-  GemmArgs a{};
-  a.R = R;
-  a.E = E;
-  a.N = N;
-  a.epilogue = W4_EPI_NONE;   // the ungated grid is the larger one
-  int nc;
-  const int64_t blocks = tiled_grid(a, &nc);
-  return align256((size_t)x_rows * (size_t)K * 2) + align256((size_t)x_rows * 4) + align256((size_t)blocks);
+  (void)R;
+  (void)E;
+  (void)N;
+  return align256((size_t)x_rows * (size_t)K * 2) + align256((size_t)x_rows * 4);
 }
 
 template <int EPI, int OUT>
-static void launch_pair(const GemmArgs& a, int64_t blocks, int ncol_blocks, uint8_t* redo, hipStream_t stream) {
-  const dim3 grid((unsigned)blocks), block(64 * NWAVES);
-  hipLaunchKernelGGL((tiled_kernel<EPI, OUT, false>), grid, block, 0, stream, a, ncol_blocks, redo);
-  hipLaunchKernelGGL((tiled_kernel<EPI, OUT, true>), grid, block, 0, stream, a, ncol_blocks, redo);
+static void launch_tiled(const GemmArgs& a, int64_t blocks, int ncol_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((tiled_kernel<EPI, OUT>), dim3((unsigned)blocks), dim3(64 * NWAVES), 0, stream, a, ncol_blocks);
 }
 
 void launch_gemm_tiled(const GemmArgs& a_in, void* ws, hipStream_t stream) {
@@ -722,17 +716,16 @@ void launch_gemm_tiled(const GemmArgs& a_in, void* ws, hipStream_t stream) {
   const size_t xe_bytes = align256((size_t)a.x_rows * 4);
   a.xh = reinterpret_cast<uint16_t*>(base);
   a.xexp = reinterpret_cast<int32_t*>(base + xh_bytes);
-  uint8_t* redo = base + xh_bytes + xe_bytes;
   if (a.x_rows > 0) {
     hipLaunchKernelGGL(rows_to_f16_kernel, dim3((unsigned)((a.x_rows + 3) / 4)), dim3(256), 0, stream, a.x, a.x_rows,
                        a.K, const_cast<uint16_t*>(a.xh), const_cast<int32_t*>(a.xexp));
   }
   int nc;
   const int64_t blocks = tiled_grid(a, &nc);
-  if (a.epilogue == W4_EPI_GEGLU_TANH) launch_pair<W4_EPI_GEGLU_TANH, W4_OUT_BF16>(a, blocks, nc, redo, stream);
-  else if (a.epilogue == W4_EPI_SWIGLU) launch_pair<W4_EPI_SWIGLU, W4_OUT_BF16>(a, blocks, nc, redo, stream);
-  else if (a.out_dtype == W4_OUT_F32) launch_pair<W4_EPI_NONE, W4_OUT_F32>(a, blocks, nc, redo, stream);
-  else launch_pair<W4_EPI_NONE, W4_OUT_BF16>(a, blocks, nc, redo, stream);
+  if (a.epilogue == W4_EPI_GEGLU_TANH) launch_tiled<W4_EPI_GEGLU_TANH, W4_OUT_BF16>(a, blocks, nc, stream);
+  else if (a.epilogue == W4_EPI_SWIGLU) launch_tiled<W4_EPI_SWIGLU, W4_OUT_BF16>(a, blocks, nc, stream);
+  else if (a.out_dtype == W4_OUT_F32) launch_tiled<W4_EPI_NONE, W4_OUT_F32>(a, blocks, nc, stream);
+  else launch_tiled<W4_EPI_NONE, W4_OUT_BF16>(a, blocks, nc, stream);
 }
 
 }  // namespace w4
