@@ -60,11 +60,11 @@ TRAFFIC = {
                     "sha256": "17f7a1b21ba9e5234e5b0e1f972c7079298534e77c268fbbcf05347057bab034",
                     "read_bytes": 141958 * 2048, "write_bytes": 725 * 1024},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "5b87418678786e3bc2558d975ade3a0275be78ca7e7b6829de7d94f30889db52",
-                     "read_bytes": 271264 * 2048, "write_bytes": 54269 * 1024},
+                     "sha256": "b37c9589d8baa783df8e7e7bd8be2275379a27b28ac621b3f43ab87f5176050d",
+                     "read_bytes": 271190 * 2048, "write_bytes": 53550 * 1024},
     "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                      "sha256": "5b87418678786e3bc2558d975ade3a0275be78ca7e7b6829de7d94f30889db52",
-                      "read_bytes": 550194 * 2048, "write_bytes": 120629 * 1024},
+                      "sha256": "b37c9589d8baa783df8e7e7bd8be2275379a27b28ac621b3f43ab87f5176050d",
+                      "read_bytes": 550266 * 2048, "write_bytes": 120559 * 1024},
 }
 
 
