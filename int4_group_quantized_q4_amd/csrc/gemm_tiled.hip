@@ -127,13 +127,17 @@ __device__ __forceinline__ int xcd_item(int b, int total) {
 // The experts' row tiles (ceil(count/BM) each, in expert order), times
 // ncol_blocks column blocks, are the work items.  Returns the item of block
 // `blk`: expert (-1 past the end), row tile inside the expert, column block.
-// Whole-wave; E <= 256.
+// Inside an expert the items run in groups of gm row tiles: a group's items
+// take the column blocks in order, and for each column block its gm row
+// tiles, so that the blocks running at once on an XCD (consecutive items)
+// share both their weight panels and their activation panels.  gm = 1: the
+// column block fastest.  Whole-wave; E <= 256.
 struct Item {
   int expert, mtile, nblock;
   int begin, end;   // the expert's sorted rows [begin, end)
 };
 
-__device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blocks, int blk) {
+__device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blocks, int gm, int blk) {
   const int lane = threadIdx.x & 63;
   int cnt[4], lo[4], hi[4], pre = 0;
 #pragma unroll
@@ -166,14 +170,15 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
   const int excl = incl - pre;
   const uint64_t bal = __ballot(lin >= excl && lin < incl);
   const int owner = __ffsll((unsigned long long)bal) - 1;
-  int e = 0, mt = 0, b = 0, en = 0;
+  int e = 0, b = 0, en = 0, tb = 0, tc = 0;
   if (lane == owner) {
     int base = excl;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (lin >= base && lin < base + cnt[s]) {
         e = lane * 4 + s;
-        mt = lin - base;
+        tb = base;
+        tc = cnt[s];
         b = lo[s];
         en = hi[s];
       }
@@ -181,10 +186,17 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
     }
   }
   it.expert = __shfl(e, owner, 64);
-  it.mtile = __shfl(mt, owner, 64);
   it.begin = __shfl(b, owner, 64);
   it.end = __shfl(en, owner, 64);
-  it.nblock = item - lin * ncol_blocks;
+  // the item's place among its expert's items: group of gm row tiles (the
+  // last group may hold fewer), then column block, then row tile
+  const int ebase = __shfl(tb, owner, 64), ecnt = __shfl(tc, owner, 64);
+  const int li = item - ebase * ncol_blocks;
+  const int g = li / (gm * ncol_blocks);
+  const int rem = li - g * gm * ncol_blocks;
+  const int gsz = ecnt - g * gm < gm ? ecnt - g * gm : gm;
+  it.nblock = rem / gsz;
+  it.mtile = g * gm + (rem - it.nblock * gsz);
   return it;
 }
 
@@ -194,7 +206,7 @@ __device__ Item find_item(const int32_t* offsets, int E, int64_t R, int ncol_blo
 // partial sum times its fp32 scale (the exact path), before the epilogue.
 template <int EPI, int OUT>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2)))
-tiled_kernel(GemmArgs a, int ncol_blocks) {
+tiled_kernel(GemmArgs a, int ncol_blocks, int gm) {
   constexpr bool GATED = EPI != W4_EPI_NONE;
   // One array per ring slot, every access naming its slot at compile time: the
   // compiler then tells the slots apart and waits, before an operand read, only
@@ -222,7 +234,7 @@ tiled_kernel(GemmArgs a, int ncol_blocks) {
   const int c = lane >> 4;
   const int64_t K = a.K, N = a.N;
 
-  const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, blockIdx.x);
+  const Item it = find_item(a.offsets, a.E, a.R, ncol_blocks, gm, blockIdx.x);
   if (it.expert < 0) return;   // uniform over the block
   const int e = __builtin_amdgcn_readfirstlane(it.expert);
   const int mt = __builtin_amdgcn_readfirstlane(it.mtile);
@@ -706,7 +718,11 @@ size_t gemm_tiled_workspace(int64_t x_rows, int64_t R, int32_t E, int64_t K, int
 
 template <int EPI, int OUT>
 static void launch_tiled(const GemmArgs& a, int64_t blocks, int ncol_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((tiled_kernel<EPI, OUT>), dim3((unsigned)blocks), dim3(64 * NWAVES), 0, stream, a, ncol_blocks);
+  // one weight matrix (a dense prefill): groups of 8 row tiles; grouped
+  // experts: the column block fastest
+  const int gm = a.E == 1 ? 8 : 1;
+  hipLaunchKernelGGL((tiled_kernel<EPI, OUT>), dim3((unsigned)blocks), dim3(64 * NWAVES), 0, stream, a, ncol_blocks,
+                     gm);
 }
 
 void launch_gemm_tiled(const GemmArgs& a_in, void* ws, hipStream_t stream) {
