@@ -60,11 +60,11 @@ TRAFFIC = {
                     "sha256": "17f7a1b21ba9e5234e5b0e1f972c7079298534e77c268fbbcf05347057bab034",
                     "read_bytes": 141958 * 2048, "write_bytes": 725 * 1024},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "b37c9589d8baa783df8e7e7bd8be2275379a27b28ac621b3f43ab87f5176050d",
-                     "read_bytes": 271190 * 2048, "write_bytes": 53550 * 1024},
+                     "sha256": "0bd93b37d99f1382f6d35ba95524ce22ddbc1421f5f2fc95daa26662b84dfc29",
+                     "read_bytes": 271123 * 2048, "write_bytes": 53635 * 1024},
     "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                      "sha256": "b37c9589d8baa783df8e7e7bd8be2275379a27b28ac621b3f43ab87f5176050d",
-                      "read_bytes": 550266 * 2048, "write_bytes": 120559 * 1024},
+                      "sha256": "0bd93b37d99f1382f6d35ba95524ce22ddbc1421f5f2fc95daa26662b84dfc29",
+                      "read_bytes": 275360 * 2048, "write_bytes": 120185 * 1024},
 }
 
 
