@@ -647,7 +647,31 @@ tiled_kernel(GemmArgs a, int ncol_blocks, int gm) {
 }
 
 // One wave per row: e = exponent putting max|x| in [2^14, 2^15), then
-// xh = fp16(x * 2^-e) (round to nearest even), xexp = e.
+// xh = fp16(x * 2^-e) (round to nearest even), xexp = e.  NCH > 0: the row
+// (at most NCH 16-byte chunks per lane) is loaded into registers at once and
+// converted from there; NCH = 0: any K, the row read twice in a loop.
+__device__ __forceinline__ int row_exponent(uint32_t m) {
+  int ex = 0;
+  if (m != 0 && m < 0x7F80u) {
+    int fe;
+    frexpf(bf16_to_f32(m), &fe);   // max|x| in [2^(fe-1), 2^fe)
+    ex = fe - 15;
+  }
+  return ex;
+}
+
+__device__ __forceinline__ u32x4 chunk_to_f16(u32x4 v, int ex) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(v[i] & 0xFFFFu), -ex);
+    const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(v[i] >> 16), -ex);
+    o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return o;
+}
+
+template <int NCH>
 __global__ void __launch_bounds__(256) rows_to_f16_kernel(const uint16_t* x, int64_t rows, int64_t K, uint16_t* xh,
                                                           int32_t* xexp) {
   const int lane = threadIdx.x & 63;
@@ -657,34 +681,44 @@ __global__ void __launch_bounds__(256) rows_to_f16_kernel(const uint16_t* x, int
   u32x4* dst = reinterpret_cast<u32x4*>(xh + row * K);
   const int nch = (int)(K / 8);
   uint32_t m = 0;
-  for (int ch = lane; ch < nch; ch += 64) {
-    const u32x4 v = src[ch];
+  if constexpr (NCH > 0) {
+    u32x4 v[NCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = max(m, v[i] & 0x7FFFu);
-      m = max(m, (v[i] >> 16) & 0x7FFFu);
+    for (int q = 0; q < NCH; ++q) {
+      const int ch = lane + 64 * q;
+      v[q] = ch < nch ? src[ch] : u32x4{0u, 0u, 0u, 0u};
     }
-  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-  int ex = 0;
-  if (m != 0 && m < 0x7F80u) {
-    int fe;
-    frexpf(bf16_to_f32(m), &fe);   // max|x| in [2^(fe-1), 2^fe)
-    ex = fe - 15;
-  }
-  for (int ch = lane; ch < nch; ch += 64) {
-    const u32x4 v = src[ch];
-    u32x4 o;
+    for (int q = 0; q < NCH; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(v[i] & 0xFFFFu), -ex);
-      const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(v[i] >> 16), -ex);
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      for (int i = 0; i < 4; ++i) {
+        m = max(m, v[q][i] & 0x7FFFu);
+        m = max(m, (v[q][i] >> 16) & 0x7FFFu);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    const int ex = row_exponent(m);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int ch = lane + 64 * q;
+      if (ch < nch) dst[ch] = chunk_to_f16(v[q], ex);
     }
-    dst[ch] = o;
+    if (lane == 0) xexp[row] = ex;
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) {
+      const u32x4 v = src[ch];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = max(m, v[i] & 0x7FFFu);
+        m = max(m, (v[i] >> 16) & 0x7FFFu);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    const int ex = row_exponent(m);
+    for (int ch = lane; ch < nch; ch += 64) dst[ch] = chunk_to_f16(src[ch], ex);
+    if (lane == 0) xexp[row] = ex;
   }
-  if (lane == 0) xexp[row] = ex;
 }
 
 }  // namespace
@@ -733,8 +767,15 @@ void launch_gemm_tiled(const GemmArgs& a_in, void* ws, hipStream_t stream) {
   a.xh = reinterpret_cast<uint16_t*>(base);
   a.xexp = reinterpret_cast<int32_t*>(base + xh_bytes);
   if (a.x_rows > 0) {
-    hipLaunchKernelGGL(rows_to_f16_kernel, dim3((unsigned)((a.x_rows + 3) / 4)), dim3(256), 0, stream, a.x, a.x_rows,
-                       a.K, const_cast<uint16_t*>(a.xh), const_cast<int32_t*>(a.xexp));
+    // 16-byte chunks per lane of one row: held in registers up to 8
+    const int64_t per_lane = (a.K / 8 + 63) / 64;
+    const dim3 grid((unsigned)((a.x_rows + 3) / 4)), block(256);
+    uint16_t* xh = const_cast<uint16_t*>(a.xh);
+    int32_t* xe = const_cast<int32_t*>(a.xexp);
+    if (per_lane <= 2) hipLaunchKernelGGL(rows_to_f16_kernel<2>, grid, block, 0, stream, a.x, a.x_rows, a.K, xh, xe);
+    else if (per_lane <= 4) hipLaunchKernelGGL(rows_to_f16_kernel<4>, grid, block, 0, stream, a.x, a.x_rows, a.K, xh, xe);
+    else if (per_lane <= 8) hipLaunchKernelGGL(rows_to_f16_kernel<8>, grid, block, 0, stream, a.x, a.x_rows, a.K, xh, xe);
+    else hipLaunchKernelGGL(rows_to_f16_kernel<0>, grid, block, 0, stream, a.x, a.x_rows, a.K, xh, xe);
   }
   int nc;
   const int64_t blocks = tiled_grid(a, &nc);

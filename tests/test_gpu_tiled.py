@@ -126,7 +126,10 @@ def test_tiled_and_streaming_agree():
     assert ok
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 256, 64), (300, 2816, 512), (129, 704, 2816)])
+# One weight matrix: items in groups of 8 row tiles of 128 (10 row tiles:
+# groups of 8 and 2; 18: 8, 8 and 2), and fewer row tiles than a group.
+@pytest.mark.parametrize("M,K,N", [(1, 256, 64), (300, 2816, 512), (129, 704, 2816), (1200, 256, 512),
+                                   (2200, 128, 1024)])
 def test_tiled_linear(M, K, N):
     rng = gen.rng_for(951, M + K + N)
     packed, sct, codes, sc = linear_weights(rng, N, K)
