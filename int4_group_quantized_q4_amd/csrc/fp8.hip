@@ -69,6 +69,25 @@ __device__ __forceinline__ int xcd_item(int b, int total) {
 }
 
 // ---------------------------------------------------------------- quantize
+// 8 bf16 values of a 16-byte chunk -> 8 E4M3 codes (two words), x / s clamped
+__device__ __forceinline__ void chunk_to_e4m3(u32x4 v, float s, uint32_t w[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f[2 * i] = fminf(fmaxf(bf16_to_f32(v[2 * h + i] & 0xFFFFu) / s, -kE4M3Max), kE4M3Max);
+      f[2 * i + 1] = fminf(fmaxf(bf16_to_f32(v[2 * h + i] >> 16) / s, -kE4M3Max), kE4M3Max);
+    }
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p, true);
+    w[h] = (uint32_t)p;
+  }
+}
+
+// NCH > 0: the row (at most NCH 16-byte chunks per lane) is loaded into
+// registers at once and quantized from there; NCH = 0: any K, read twice.
+template <int NCH>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
@@ -76,37 +95,54 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
   if (row >= rows) return;
   const u32x4* src = reinterpret_cast<const u32x4*>(x + row * K);
   const int nch = (int)(K / 8);   // 8 values per 16-byte chunk
+  uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * K);
   uint32_t m = 0;
-  for (int ch = lane; ch < nch; ch += 64) {
-    const u32x4 v = src[ch];
+  u32x4 v[NCH > 0 ? NCH : 1];
+  if constexpr (NCH > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = max(m, v[i] & 0x7FFFu);
-      m = max(m, (v[i] >> 16) & 0x7FFFu);
+    for (int k = 0; k < NCH; ++k) {
+      const int ch = lane + 64 * k;
+      v[k] = ch < nch ? src[ch] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = max(m, v[k][i] & 0x7FFFu);
+        m = max(m, (v[k][i] >> 16) & 0x7FFFu);
+      }
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) {
+      const u32x4 c = src[ch];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = max(m, c[i] & 0x7FFFu);
+        m = max(m, (c[i] >> 16) & 0x7FFFu);
+      }
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
   const float amax = bf16_to_f32(m);
   const float s = amax > 0.f ? amax / kE4M3Max : 1.0f;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * K);
-  for (int ch = lane; ch < nch; ch += 64) {
-    const u32x4 v = src[ch];
-    uint32_t w[2];
+  if constexpr (NCH > 0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float f[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f[2 * i] = fminf(fmaxf(bf16_to_f32(v[2 * h + i] & 0xFFFFu) / s, -kE4M3Max), kE4M3Max);
-        f[2 * i + 1] = fminf(fmaxf(bf16_to_f32(v[2 * h + i] >> 16) / s, -kE4M3Max), kE4M3Max);
+    for (int k = 0; k < NCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+        uint32_t w[2];
+        chunk_to_e4m3(v[k], s, w);
+        dst[2 * ch] = w[0];
+        dst[2 * ch + 1] = w[1];
       }
-      int p = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      p = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p, true);
-      w[h] = (uint32_t)p;
     }
-    dst[2 * ch] = w[0];
-    dst[2 * ch + 1] = w[1];
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) {
+      uint32_t w[2];
+      chunk_to_e4m3(src[ch], s, w);
+      dst[2 * ch] = w[0];
+      dst[2 * ch + 1] = w[1];
+    }
   }
   if (lane == 0) scale[row] = s;
 }
@@ -577,7 +613,13 @@ void launch_fp8_gemm(const Fp8Args& a, hipStream_t stream) {
 
 void launch_fp8_quant_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* q, float* scale, hipStream_t stream) {
   if (rows <= 0) return;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, x, rows, K, q, scale);
+  // 16-byte chunks per lane of one row: held in registers up to 8
+  const int64_t per_lane = (K / 8 + 63) / 64;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (per_lane <= 2) hipLaunchKernelGGL(quant_rows_kernel<2>, grid, block, 0, stream, x, rows, K, q, scale);
+  else if (per_lane <= 4) hipLaunchKernelGGL(quant_rows_kernel<4>, grid, block, 0, stream, x, rows, K, q, scale);
+  else if (per_lane <= 8) hipLaunchKernelGGL(quant_rows_kernel<8>, grid, block, 0, stream, x, rows, K, q, scale);
+  else hipLaunchKernelGGL(quant_rows_kernel<0>, grid, block, 0, stream, x, rows, K, q, scale);
 }
 
 }  // namespace w4
