@@ -179,17 +179,20 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   bool active;
   const uint8_t* wb;
   const uint16_t* sb;
-  auto set_tiles = [&](int ts) __attribute__((always_inline)) {
+  auto tiles_for = [&](int ts, int& u, int& t, bool& act) __attribute__((always_inline)) {
     const int u0 = (wgi * tsets + ts) * PER_WG;
     if constexpr (GATED) {
-      unit = u0 + (wv >> 1);                           // gate/up pair
-      tile = unit + ((wv & 1) ? (int)(N / 32) : 0);    // the up tile sits N/2 rows below
+      u = u0 + (wv >> 1);                           // gate/up pair
+      t = u + ((wv & 1) ? (int)(N / 32) : 0);       // the up tile sits N/2 rows below
     } else {
-      unit = u0 + wv;
-      tile = unit;
+      u = u0 + wv;
+      t = u;
     }
-    active = unit < units_per_expert;
-    if (!active) tile = 0;
+    act = u < units_per_expert;
+    if (!act) t = 0;
+  };
+  auto set_tiles = [&](int ts) __attribute__((always_inline)) {
+    tiles_for(ts, unit, tile, active);
     wb = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)tile * 8 * K;
     sb = a.scales + ((int64_t)e * N + (int64_t)tile * kTileRows) * G;
   };
@@ -203,9 +206,15 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   int64_t row_begin = 0, row_end = a.R;
   // The first pass's weight ring does not depend on the rows: it is issued
   // before the row range is known (ids scan or offsets read) and that wait
-  // overlaps the weight stream's first latency.  Later passes load their ring
-  // in their own prologue, after the barrier that ends the previous pass.
-  // (The ids go out first: the scan must not wait for the ring to land.)
+  // overlaps the weight stream's first latency.  Every later pass (of the
+  // same tile or of the next unit set's) gets its ring and its first scale
+  // span from the pass before it: the last D refills of a pass load the next
+  // pass's blocks 0 .. D-1 (block b sits in ring slot b % D, so the slots
+  // they free are exactly the ones those blocks go to), and the span goes to
+  // registers after the pass's span loop.  Only registers are loaded early;
+  // the span reaches its LDS buffer in the next pass's prologue, after the
+  // barrier, as before.  (The ids go out first: the scan must not wait for
+  // the ring to land.)
   int idv[8];
   float lgv[RM == 2 ? kLogitsPerWave : 1][2];
   const int ntok = (int)a.R / a.kslots;   // (logits mode: R <= 64 k)
@@ -259,12 +268,14 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
   uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
-  auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) {
+  auto span_load_at = [&](u32x4* t, uint32_t sv, int sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i)
       t[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           srs, sv_lane, (uint32_t)(SPBYTES * sp + 1024 * i), 0));
+                                           srs, sv, (uint32_t)(SPBYTES * sp + 1024 * i), 0));
   };
+  auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) { span_load_at(t, sv_lane, sp); };
+  u32x4 snx[SPL];   // the next pass's first scale span, loaded during this pass
   auto span_store = [&](const u32x4* t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) *reinterpret_cast<u32x4*>(mys + 1024 * i + 16 * lane) = t[i];
@@ -281,17 +292,11 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     if (u0 >= units_per_expert) break;   // uniform over the workgroup
     sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
   }
-  // the partial last block (1..3 groups), loaded once per set
+  // the partial last block (1..3 groups), loaded once per set, in its first
+  // pass after the prologue's barrier (used at the pass's end only: loaded
+  // earlier, the prologue's waits would include it)
   uint32_t ct[3] = {0u, 0u, 0u};
   float st[3] = {0.f, 0.f, 0.f};
-  if (gtail > 0) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < gtail) {
-        ct[j] = *reinterpret_cast<const uint32_t*>(wb + 1024 * (int64_t)NBF + 4 * gtail * lane + 4 * j);
-        st[j] = bf16_to_f32(sb[64 * (int64_t)NBF + r * gtail + j]);
-      }
-  }
 
   // Activation staging: chunk ch (columns [ch*KC, ch*KC+KC)) of the pass's rows
   // goes to LDS buffer ch%2.  The global loads of chunk ch+1 are issued before
@@ -368,21 +373,46 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       }
     };
 
-    // every load of the pass's start is issued before the first wait: the
-    // first chunk's activations, the first scale span, the ring's blocks
+    // The pass after this one, whose ring and first span this pass loads:
+    // another pass over the same tile, the next unit set's tile, or none
+    // (uniform over the wave).
+    const uint8_t* wnx = nullptr;
+    uint32_t svnx = 0u;
+    if (row0 + 16 * MAXT < row_end) {
+      wnx = wb;
+      svnx = sv_lane;
+    } else if (ts + 1 < tsets && (wgi * tsets + ts + 1) * PER_WG < units_per_expert) {
+      int u2, t2;
+      bool a2;
+      tiles_for(ts + 1, u2, t2, a2);
+      wnx = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)t2 * 8 * K;
+      svnx = (uint32_t)t2 * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
+    }
+    const bool first_pass = ts == 0 && row0 == row_begin;
+
+    // the first chunk's activations are the only load the prologue waits for
+    // (the first pass's span is loaded here too; later passes' came earlier)
     __syncthreads();   // the previous pass is done with both buffers
     stage_load(0);
     if (NBF > 0) {
-      u32x4 s0[SPL];
-      span_load(s0, 0);
-      if (ts > 0 || row0 != row_begin) {   // (the first pass's ring is already in flight)
-#pragma unroll
-        for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+      if (first_pass) {
+        u32x4 s0[SPL];
+        span_load(s0, 0);
+        span_store(s0);
+      } else {
+        span_store(snx);
       }
-      span_store(s0);
     }
     stage_store(0);
     __syncthreads();
+    if (gtail > 0 && row0 == row_begin) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < gtail) {
+          ct[j] = *reinterpret_cast<const uint32_t*>(wb + 1024 * (int64_t)NBF + 4 * gtail * lane + 4 * j);
+          st[j] = bf16_to_f32(sb[64 * (int64_t)NBF + r * gtail + j]);
+        }
+    }
 
     int arow[MAXT];   // LDS row of this lane's A operand (padding rows read row 0)
 #pragma unroll
@@ -393,7 +423,9 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     for (int tt = 0; tt < MAXT; ++tt) acc[tt] = zero4;
 
     // one block: MFMAs on the slot's codes, then refill the slot with block bn
-    // (after the slot's last use, so no register copies are needed)
+    // (after the slot's last use, so no register copies are needed); past
+    // the tile's last block, with block `slot` of the next pass (none: the
+    // last block again, never used)
     auto do_block = [&](const uint8_t* xb, const float* tb, int b, int lb, int slot, int bn)
                         __attribute__((always_inline)) {
       const u32x2 sv = *reinterpret_cast<const u32x2*>(mys + (b % SPB) * 128 + 8 * r);
@@ -416,7 +448,10 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       // block's MFMA results stay live until the end of the chunk
 #pragma unroll
       for (int tt = 0; tt < MAXT; ++tt) asm volatile("" : "+v"(acc[tt]));
-      load_block(slot, bn);
+      const uint8_t* src = bn < NBF ? wb + 1024 * (int64_t)bn
+                                    : (wnx ? wnx + 1024 * (int64_t)(slot < NBF ? slot : NBF - 1)
+                                           : wb + 1024 * (int64_t)(NBF - 1));
+      cw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * lane));
       __builtin_amdgcn_sched_barrier(0);   // issue the refill here, not later
     };
 
@@ -433,8 +468,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       const float* tb = ctab + (ch & 1) * (CB * 4 * TROWS);
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb) {
-        const int bn = ch * CB + lb + D;
-        do_block(xb, tb, ch * CB + lb, lb, lb % D, bn < NBF ? bn : NBF - 1);
+        do_block(xb, tb, ch * CB + lb, lb, lb % D, ch * CB + lb + D);
       }
       stage_store(chn);
       __syncthreads();
@@ -450,6 +484,9 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       for (int k = 0; k < CPS; ++k) do_chunk(sp * CPS + k);
       span_store(snext);
     }
+    // the next pass's first span (its registers are free from here on; with
+    // no next pass, a span that is never used)
+    if (NBF > 0) span_load_at(snx, svnx, 0);
     // the remaining full chunks, in the span parked last
     for (int ch = nspan_full * CPS; ch < nfull; ++ch) do_chunk(ch);
     // the last, partial chunk: remaining full blocks and the partial block
@@ -459,7 +496,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       const float* tb = ctab + (ch & 1) * (CB * 4 * TROWS);
 #pragma unroll
       for (int lb = 0; lb < CB; ++lb)
-        if (ch * CB + lb < NBF) do_block(xb, tb, ch * CB + lb, lb, lb % D, NBF - 1);
+        if (ch * CB + lb < NBF) do_block(xb, tb, ch * CB + lb, lb, lb % D, ch * CB + lb + D);
       if (gtail > 0) {
         const int lb = NBF - ch * CB;   // local index of the partial block
 #pragma unroll
