@@ -243,9 +243,11 @@ def moe_inputs(cfg, seed_base=0):
     return x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s)
 
 
-def check_layer(cfg, label, ties=False):
+def check_layer(cfg, label, ties=False, bump=()):
     T, d, I, E, k = cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"]
     x, logits, (w1p, w1t, w1c, w1s), (w2p, w2t, w2c, w2s) = moe_inputs(cfg)
+    for e, t0, t1 in bump:                               # expert e in the top-k of tokens t0 .. t1-1
+        logits[t0:t1, e] += 20.0
     if ties:
         logits[0, :] = 0.5                               # a row of ties: ids 0..k-1
         if T > 5:
@@ -286,6 +288,17 @@ def test_moe_layer_decode_both_paths(kernel):
     cfg = dict(gen.MOE_DECODE, id=942)
     with w4.gemm_kernel(kernel):
         assert check_layer(cfg, "moe-decode kernel=%d" % kernel) == (kernel == w4.W4_KERNEL_TILED)
+
+
+def test_moe_layer_decode_popular_experts():
+    """The 64-token layer (4 rows per expert on average, so each gate/up
+    workgroup takes several unit sets in turn) with three experts far above
+    the average: 40 rows (16-row passes of 16, 16 and 8), 20 rows (16 and 4)
+    and 21 rows (16 and 5).  Each pass loads the next pass's weight ring and first
+    scale span, and here a pass's successor is another pass over the same
+    tiles as well as the next unit set's tiles."""
+    cfg = dict(gen.MOE_DECODE, id=943)
+    assert not check_layer(cfg, "moe-decode, popular experts", bump=((5, 0, 40), (77, 20, 38), (126, 47, 64)))
 
 
 @pytest.mark.parametrize("T", [1, 40, 64])
