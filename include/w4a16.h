@@ -359,9 +359,12 @@ int w4a16_moe_combine(const void* o, int32_t o_dtype, const int32_t* row_to_sort
  *              gate/up matmul (top-k and rows from the logits),
  *              w4a16_moe_gmm_ids for the down matmul (row_div = 1), then
  *              w4a16_moe_combine (row r = t*k + j): no sort;
- *   sorted     the full routing plan of w4a16_moe_route, then the two matmuls
- *              gather their rows through it, then w4a16_moe_combine.
- * Both store the intermediates a and o at the routed rows r = t*k + j.
+ *   sorted     the full routing plan of w4a16_moe_route, then the gate/up
+ *              matmul gathers its x rows through it, the down matmul reads
+ *              a's rows in sorted order, then w4a16_moe_combine.
+ * Both store o at the routed rows r = t*k + j.  The streaming path stores a
+ * at the routed rows too, the sorted path at the sorted positions (a's row i
+ * belongs to routed row sorted_rows[i]).
  *   x       in  [T][d] bf16;  logits in [T][E] fp32
  *   w1_q    in  E * (2I)*d/2 bytes tile16 (rows [0, I) gate, [I, 2I) up);
  *   w1_s    in  E * 2I*d/32 bf16, tile16 scale layout

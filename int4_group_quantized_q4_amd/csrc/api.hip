@@ -470,17 +470,19 @@ int w4a16_moe_layer(const uint16_t* x, const float* logits, int64_t T, int32_t E
     w4::launch_combine(o, W4_OUT_F32, nullptr, wts, T, k, d, y, stream);
     return launch_status();
   }
-  // Many rows per expert: the routing plan sorts the rows by expert; the
-  // matmuls gather their rows through it and store a and o at the rows' own
-  // (routed) positions, where the combine reads them.
+  // Many rows per expert: the routing plan sorts the rows by expert.  The
+  // gate/up matmul gathers its x rows through it and stores a in sorted
+  // order, so the down matmul reads each expert's rows contiguously (its
+  // first activation loads wait for no index load) and stores o at the rows'
+  // own (routed) positions, where the combine reads them.
   st = w4a16_moe_route(logits, T, E, k, ids, wts, offs, srows, stoks, r2s, rws, p[7] - p[6], stream);
   if (st != W4_OK) return st;
   a1.row_index = stoks;
   a1.offsets = offs;
-  a1.out_index = srows;
+  a1.out_index = nullptr;
   st = run_gemm(a1, gws, gws_bytes, stream);
   if (st != W4_OK) return st;
-  a2.row_index = srows;
+  a2.row_index = nullptr;
   a2.offsets = offs;
   a2.out_index = srows;
   st = run_gemm(a2, gws, gws_bytes, stream);

@@ -265,9 +265,11 @@ def check_layer(cfg, label, ties=False, bump=()):
     if views["sorted"]:   # the sort outputs exist on the sorted path only
         assert np.array_equal(views["expert_offsets"].cpu().numpy(), plan["offsets"])
         assert np.array_equal(views["sorted_tokens"].cpu().numpy(), plan["tokens"])
-    # a and o are stored at the routed rows r = t*k + j; the oracle's follow the sort
+    # o is stored at the routed rows r = t*k + j, a too on the streaming path
+    # and in sorted order on the sorted path; the oracle's follow the sort
+    a_ref = ref["a"] if views["sorted"] else ref["a"][plan["inv"]]
     a_ok, a_mx, a_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(views["a"])),
-                                                oracle.bf16_bits_to_f64(ref["a"][plan["inv"]]))
+                                                oracle.bf16_bits_to_f64(a_ref))
     o_ok, o_mx, o_rms = oracle.within_tolerance(views["o"].cpu().numpy(), ref["o"][plan["inv"]])
     y_ok, y_mx, y_rms = oracle.within_tolerance(oracle.bf16_bits_to_f64(bits_host(y)),
                                                 oracle.bf16_bits_to_f64(ref["y"]))
