@@ -61,7 +61,7 @@ TRAFFIC = {
                     "read_bytes": 139675 * 2048, "write_bytes": 725 * 1024},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
                      "sha256": "4729a9e29ec30da2192860a67523fb9ae5f2a4f3fd9674fd5a15e2dd55725244",
-                     "read_bytes": 271213 * 2048, "write_bytes": 53591 * 1024},
+                     "read_bytes": 271193 * 2048, "write_bytes": 53697 * 1024},
     "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
                       "sha256": "4729a9e29ec30da2192860a67523fb9ae5f2a4f3fd9674fd5a15e2dd55725244",
                       "read_bytes": 275319 * 2048, "write_bytes": 119939 * 1024},
