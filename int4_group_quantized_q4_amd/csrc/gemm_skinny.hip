@@ -203,10 +203,38 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     cw[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + 1024 * (int64_t)b + 16 * lane));
   };
 
+  // Scales of the full blocks travel in spans of SPB blocks (contiguous in the
+  // tile's scale layout): 128-bit loads, one per lane per 8 blocks, parked in
+  // this wave's LDS span buffer, then 8 bytes per lane per block from there.
+  // The next span overwrites the buffer after the wave's last read of the
+  // current one (LDS accesses of one wave complete in order).  Per-block
+  // 128-byte scale loads would make a second, sparse stream beside the codes.
+  // The loads go through a buffer descriptor over the expert's scales: lanes
+  // past the tile's last full block read the tail block or the next tile, and
+  // past the end of the expert get zeros; those bytes are never used.
+  uint8_t* mys = ssc + wv * SPBYTES;
+  const int NSP = (NBF + SPB - 1) / SPB;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
+  uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
+  auto span_load_at = [&](u32x4* t, uint32_t sv, int sp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      t[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           srs, sv, (uint32_t)(SPBYTES * sp + 1024 * i), 0));
+  };
+  auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) { span_load_at(t, sv_lane, sp); };
+  u32x4 snx[SPL];   // the next pass's first scale span, loaded during this pass
+  auto span_store = [&](const u32x4* t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) *reinterpret_cast<u32x4*>(mys + 1024 * i + 16 * lane) = t[i];
+  };
+
   int64_t row_begin = 0, row_end = a.R;
-  // The first pass's weight ring does not depend on the rows: it is issued
-  // before the row range is known (ids scan or offsets read) and that wait
-  // overlaps the weight stream's first latency.  Every later pass (of the
+  // The first pass's weight ring and first scale span do not depend on the
+  // rows: they are issued before the row range is known (ids scan or offsets
+  // read) and that wait overlaps the weight stream's first latency.  Every
+  // later pass (of the
   // same tile or of the next unit set's) gets its ring and its first scale
   // span from the pass before it: the last D refills of a pass load the next
   // pass's blocks 0 .. D-1 (block b sits in ring slot b % D, so the slots
@@ -226,6 +254,7 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
   if (NBF > 0) {
 #pragma unroll
     for (int i = 0; i < D; ++i) load_block(i, i < NBF ? i : NBF - 1);
+    span_load(snx, 0);
   }
   if constexpr (RM == 1) {
     row_end = __builtin_amdgcn_readfirstlane(
@@ -253,33 +282,6 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
     else return a.out_index ? (int64_t)a.out_index[i] : i;
   };
 
-
-  // Scales of the full blocks travel in spans of SPB blocks (contiguous in the
-  // tile's scale layout): 128-bit loads, one per lane per 8 blocks, parked in
-  // this wave's LDS span buffer, then 8 bytes per lane per block from there.
-  // The next span overwrites the buffer after the wave's last read of the
-  // current one (LDS accesses of one wave complete in order).  Per-block
-  // 128-byte scale loads would make a second, sparse stream beside the codes.
-  // The loads go through a buffer descriptor over the expert's scales: lanes
-  // past the tile's last full block read the tail block or the next tile, and
-  // past the end of the expert get zeros; those bytes are never used.
-  uint8_t* mys = ssc + wv * SPBYTES;
-  const int NSP = (NBF + SPB - 1) / SPB;
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.scales + (int64_t)e * N * G), 0, (int)(N * G * 2), kRsrcFlags);
-  uint32_t sv_lane = (uint32_t)tile * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
-  auto span_load_at = [&](u32x4* t, uint32_t sv, int sp) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      t[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           srs, sv, (uint32_t)(SPBYTES * sp + 1024 * i), 0));
-  };
-  auto span_load = [&](u32x4* t, int sp) __attribute__((always_inline)) { span_load_at(t, sv_lane, sp); };
-  u32x4 snx[SPL];   // the next pass's first scale span, loaded during this pass
-  auto span_store = [&](const u32x4* t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) *reinterpret_cast<u32x4*>(mys + 1024 * i + 16 * lane) = t[i];
-  };
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -388,21 +390,11 @@ __global__ void __launch_bounds__(64 * kWaves) W4_DECODE_OCC decode_kernel(GemmA
       wnx = a.qweight + (int64_t)e * (N * K / 2) + (int64_t)t2 * 8 * K;
       svnx = (uint32_t)t2 * (uint32_t)(32 * G) + 16u * (uint32_t)lane;
     }
-    const bool first_pass = ts == 0 && row0 == row_begin;
-
     // the first chunk's activations are the only load the prologue waits for
-    // (the first pass's span is loaded here too; later passes' came earlier)
+    // (the pass's ring and first span were loaded earlier)
     __syncthreads();   // the previous pass is done with both buffers
     stage_load(0);
-    if (NBF > 0) {
-      if (first_pass) {
-        u32x4 s0[SPL];
-        span_load(s0, 0);
-        span_store(s0);
-      } else {
-        span_store(snx);
-      }
-    }
+    if (NBF > 0) span_store(snx);
     stage_store(0);
     __syncthreads();
     if (gtail > 0 && row0 == row_begin) {
