@@ -53,17 +53,18 @@ EXPERT_W2_BYTES = 2816 * 704 // 2 + 2816 * 22 * 2    # 1,115,136
 # HBM bytes per launch of the two roofline kernels, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE passes over this bench (profiles/gemm_hbm_traffic.md): reads scaled
 # by 2.000 and writes by 1.000, the factors a 512 MiB device copy gives.  They
-# hold only for the sources they were taken on (sha256 of the listed files in
-# csrc/, in order); once one changes, the bench reports traffic as null.
+# hold only for the code they were taken on (sha256 of the listed files in
+# csrc/, in order, comments and blank lines removed: sources_sha256); once
+# that code changes, the bench reports traffic as null.
 TRAFFIC = {
     "decode_gmm1": {"sources": ("gemm_skinny.hip", "common.h", "internal.h"),
-                    "sha256": "f68c3b73aea5115a630c5da43e7a22a4e23a678f99a7cd2f108cf077986e2719",
+                    "sha256": "8ed30d9d7c51d6629fbed711f76b9ee8b1e817372d5a07ff715cf975866c3c70",
                     "read_bytes": 139715 * 2048, "write_bytes": 725 * 1024},
     "prefill_gmm1": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                     "sha256": "4729a9e29ec30da2192860a67523fb9ae5f2a4f3fd9674fd5a15e2dd55725244",
+                     "sha256": "1297ca20c60924a20d5a114d81e548aebc010fe3668275c0cbb80123a0a7d019",
                      "read_bytes": 271193 * 2048, "write_bytes": 53697 * 1024},
     "dense_prefill": {"sources": ("gemm_tiled.hip", "common.h", "internal.h"),
-                      "sha256": "4729a9e29ec30da2192860a67523fb9ae5f2a4f3fd9674fd5a15e2dd55725244",
+                      "sha256": "1297ca20c60924a20d5a114d81e548aebc010fe3668275c0cbb80123a0a7d019",
                       "read_bytes": 275319 * 2048, "write_bytes": 119939 * 1024},
 }
 
@@ -71,19 +72,30 @@ TRAFFIC = {
 def traffic_source(key):
     rec = TRAFFIC[key]
     return ("rocprofv3 FETCH_SIZE and WRITE_SIZE counter passes (profiles/gemm_hbm_traffic.md) taken on kernel "
-            "sources sha256 %s...; null once those sources change" % rec["sha256"][:12])
+            "sources' code sha256 %s...; null once that code changes" % rec["sha256"][:12])
+
+
+def sources_sha256(files):
+    """sha256 of the listed csrc/ files with their comments and blank lines
+    removed, so that only a change of code invalidates a counter figure."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "int4_group_quantized_q4_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+        h.update(code.encode())
+    return h.hexdigest()
 
 
 def traffic_of(key):
     """Counter-measured HBM bytes (read + write) per launch, or None when the
-    kernel's sources differ from those the counters were taken on."""
-    import hashlib
+    kernel's code differs from the code the counters were taken on."""
     rec = TRAFFIC[key]
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        with open(os.path.join(ROOT, "int4_group_quantized_q4_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest() != rec["sha256"]:
+    if sources_sha256(rec["sources"]) != rec["sha256"]:
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 

@@ -39,9 +39,11 @@
 // matrix's last column block the waves left without weight tiles skip the
 // expansion and the MFMAs (they still stage activations and meet the
 // barriers).
-// Scheduling: block b takes item (expert, row tile, column block) with the
-// column block fastest, dealt so that consecutive items share an XCD and its
-// L2: the row tile's activations and the expert's weights are re-read from L2.
+// Scheduling: block b takes item (expert, row tile, column block), dealt so
+// that consecutive items share an XCD and its L2: for grouped experts the
+// column block fastest (the row tile's activations and the expert's weights
+// are re-read from L2); for one weight matrix, groups of 8 row tiles with the
+// column block outer, so the blocks running together share weight panels too.
 
 #include <type_traits>
 
