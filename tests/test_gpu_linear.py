@@ -157,10 +157,10 @@ def test_linear_fused_splitk_matches_two_kernel_sum_order():
 
 def test_linear_dense_prefill_with_zero_groups_full_size():
     """All-zero groups as the repack emits them (codes 0, scale +0: ±0 is
-    outside fp16's exact range for s*q, so every block holding one is redone
-    by the exact kernel) scattered over 1% of the groups of the full
-    prefill-shaped matrix: the exact relaunch at full size, 24 sampled rows
-    against the oracle."""
+    outside fp16's exact range for s*q, so every block holding one
+    recomputes its tile on the exact path, in the same launch) scattered over
+    1% of the groups of the full prefill-shaped matrix: the exact path at
+    full size, 24 sampled rows against the oracle."""
     import layout
     cfg = gen.DENSE_PREFILL
     M, K, N = cfg["M"], cfg["K"], cfg["N"]
